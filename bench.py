@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled 4-bit quantized-matmul hot path on one MI355X.
+
+One step is one pass over every stage of the path on synthetic input that is
+already resident in HBM:
+
+  act_quant   NVFP4 activation quantize X[4096,5120] (tensor amax + codes +
+              E4M3 scales + global scale), 1 % outliers at +-20
+  dequant     NVFP4 dequantize of the same tensor
+  w_quant     MXFP4 quantize W[5760,2880] and affine quantize W[1024,512]
+  qmv_sweep   affine g64 decode GEMV over 64 layers x {gate, up, down}
+              ([25600,5120], [25600,5120], [5120,25600]): 192 distinct matrices,
+              14.17 GB of packed weights (more than the 256 MB Infinity Cache)
+  qmv_fp4     MXFP4 qmv W[5760,2880] at M = 1 and 8, NVFP4 qmv [25600,5120] M=1
+  qqmm        NVFP4 prefill X[2048,5120] . W[25600,5120]^T (x quantized on the
+              fly, alpha = g_x g_w), the headline GEMM
+  qqmm_1134 / qqmm_4096   the same GEMM at M = 1134 and 4096
+  qmm_mx      MXFP4 qq GEMM on the scaled MFMA, M = 32 and 512
+  qmm_affine  affine weight-only x[2048,5120] . W_up[25600,5120]^T
+
+The JSON line reports the headline metric: `value` is the sustained qmv GB/s
+of the 64-layer sweep (algorithmic bytes: packed codes + scales + biases +
+x + y per matrix); `qmm_tflops` the NVFP4 qqmm TFLOP/s at M = 2048 (GEMM
+kernel alone and with the activation quantize).  `roofline` is for the qmv
+kernel (HBM), `roofline_qmm` for the qqmm GEMM kernel (fp16 MFMA).
+`cpu_baseline` times the CPU oracle on a bounded sample.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16 / bf16 MFMA, vendor figure
+FP4_PEAK_TFS = 10100.0       # MI355X dense MXFP4 MFMA, vendor figure
+
+HIDDEN, INTER, LAYERS = 5120, 25600, 64
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma-separated stage names (profiling)")
+    return p.parse_args()
+
+
+def affine_bytes(N, K, M=1):
+    """Algorithmic bytes of one affine qmv: codes + scales + biases + x + y."""
+    return N * K // 2 + 2 * 2 * N * (K // 64) + 2 * M * K + 2 * M * N
+
+
+def fp4_bytes(N, K, G, M=1):
+    return N * K // 2 + N * (K // G) + 2 * M * K + 2 * M * N
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by weight rows; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_bit_fp_amd as b
+    import synth_inputs as S
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count} lib={b.version()}")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------- inputs
+    t_setup = time.time()
+    X_act = to_dev(S.nvfp4_activations())                        # [4096, 5120]
+    q_act = b.empty_quantized(b.NVFP4, 4096, HIDDEN, dev)
+    dq_act = torch.empty((4096, HIDDEN), dtype=torch.bfloat16, device=dev)
+    W_mx_bf = to_dev(S.mxfp4_weights())                          # [5760, 2880]
+    q_mx = b.quantize(W_mx_bf, b.MXFP4)
+    q_mx_out = b.empty_quantized(b.MXFP4, 5760, 2880, dev)
+    _, w_small = S.affine_small()
+    W_small = to_dev(w_small)
+    q_small_out = b.empty_quantized(b.AFFINE, 1024, 512, dev)
+
+    x_dec = to_dev(S.generic((1, HIDDEN), 1.0, seed=3))
+    x_dec_down = to_dev(S.generic((1, INTER), 1.0, seed=3, stream=9))
+    sweep = []  # (x, q, y)
+    for layer in range(LAYERS):
+        for name, (N, K) in (("gate", (INTER, HIDDEN)), ("up", (INTER, HIDDEN)),
+                             ("down", (HIDDEN, INTER))):
+            seed = 1000 + 3 * layer + {"gate": 0, "up": 1, "down": 2}[name]
+            wb = S.torch_normal_bf16((N, K), 0.02, seed, dev)
+            q = b.quantize(wb, b.AFFINE)
+            del wb
+            x = x_dec if K == HIDDEN else x_dec_down
+            sweep.append((x, q, torch.empty((1, N), dtype=torch.bfloat16, device=dev)))
+    sweep_bytes = sum(affine_bytes(q.rows, q.cols) for _, q, _ in sweep)
+
+    x_mx = {M: to_dev(S.mxfp4_activations(M)) for M in (1, 8, 32, 512)}
+    y_mx = {M: torch.empty((M, 5760), dtype=torch.bfloat16, device=dev) for M in (1, 8, 32, 512)}
+    ws_mx = {M: torch.empty(b.qmm_workspace_bytes(b.MXFP4, M, 2880, "same"), dtype=torch.uint8,
+                            device=dev) for M in (32, 512)}
+
+    Wp = S.torch_normal_bf16((INTER, HIDDEN), 0.02, 55, dev)      # prefill weights
+    q_pf = b.quantize(Wp, b.NVFP4)
+    del Wp
+    x_nv1 = to_dev(S.generic((1, HIDDEN), 1.0, seed=8))
+    y_nv1 = torch.empty((1, INTER), dtype=torch.bfloat16, device=dev)
+    X_pf = {M: S.torch_normal_bf16((M, HIDDEN), 0.02, 500 + M, dev) for M in (1134, 2048, 4096)}
+    Y_pf = {M: torch.empty((M, INTER), dtype=torch.bfloat16, device=dev) for M in X_pf}
+    ws_pf = {M: torch.empty(b.qmm_workspace_bytes(b.NVFP4, M, HIDDEN, "same"), dtype=torch.uint8,
+                            device=dev) for M in X_pf}
+    X_aff = S.torch_normal_bf16((2048, HIDDEN), 1.0, 6, dev)
+    Y_aff = torch.empty((2048, INTER), dtype=torch.bfloat16, device=dev)
+    q_up0 = sweep[1][1]
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t_setup:.1f}s; sweep {len(sweep)} matrices, "
+        f"{sweep_bytes / 1e9:.2f} GB")
+
+    # ------------------------------------------------------------- stages
+    def st_act_quant():
+        b.quantize(X_act, b.NVFP4, "compute", out=q_act)
+
+    def st_dequant():
+        b.dequantize(q_act, out=dq_act)
+
+    def st_w_quant():
+        b.quantize(W_mx_bf, b.MXFP4, out=q_mx_out)
+        b.quantize(W_small, b.AFFINE, out=q_small_out)
+
+    def st_qmv_sweep():
+        for x, q, y in sweep:
+            b.qmv(x, q, out=y)
+
+    def st_qmv_fp4():
+        b.qmv(x_mx[1], q_mx, out=y_mx[1])
+        b.qmv(x_mx[8], q_mx, out=y_mx[8])
+        b.qmv(x_nv1, q_pf, out=y_nv1)
+
+    def qq(M):
+        return lambda: b.qmm(X_pf[M], q_pf, act="same", workspace=ws_pf[M], out=Y_pf[M])
+
+    def st_qmm_mx():
+        for M in (32, 512):
+            b.qmm(x_mx[M], q_mx, act="same", workspace=ws_mx[M], out=y_mx[M])
+
+    def st_qmm_affine():
+        b.qmm(X_aff, q_up0, act="bf16", out=Y_aff)
+
+    stages = [("act_quant", st_act_quant), ("dequant", st_dequant), ("w_quant", st_w_quant),
+              ("qmv_sweep", st_qmv_sweep), ("qmv_fp4", st_qmv_fp4), ("qqmm", qq(2048)),
+              ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qmm_mx", st_qmm_mx),
+              ("qmm_affine", st_qmm_affine)]
+    if args.only:
+        keep = set(args.only.split(","))
+        stages = [s for s in stages if s[0] in keep]
+    names = [n for n, _ in stages]
+
+    stream = torch.cuda.current_stream()
+    ev = {n: [] for n in names}
+
+    def step(record):
+        for n, fn in stages:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[n].append((e0, e1))
+            else:
+                fn()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms = {n: float(np.median([a.elapsed_time(c) for a, c in ev[n]])) for n in names}
+    log("[bench] stage medians (ms): " + ", ".join(f"{n}={ms[n]:.3f}" for n in names))
+
+    out = {"metric": "qmv achieved HBM GB/s (M=1, 4-bit) + qmm TFLOPS at M=2048; % of roofline",
+           "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u4 codes, bf16/fp16 MFMA, fp32 acc",
+           "data": "synthetic (seeded normal inputs; weights quantized on the GPU)",
+           "config": {"workload": "affine 4-bit g64 decode qmv sweep, 64 layers x "
+                                  "{gate,up,down} of hidden 5120 / intermediate 25600 "
+                                  "(14.17 GB), plus NVFP4 prefill qqmm X[2048,5120] . "
+                                  "W[25600,5120]^T and the other hot-path stages",
+                      "arch": "gfx950", "device": props.name}}
+    stage_ms = {n: round(v, 4) for n, v in ms.items()}
+    out["stages_ms"] = stage_ms
+    if "qmv_sweep" in ms:
+        gbs = sweep_bytes / (ms["qmv_sweep"] * 1e-3) / 1e9
+        out["value"] = round(gbs, 1)
+        out["qmv_sweep_gbs"] = round(gbs, 1)
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "qmv_kernel (affine, M=1)",
+                           "note": "algorithmic bytes / sweep time (192 back-to-back launches)"}
+    if "qqmm" in ms:
+        flop = 2.0 * 2048 * INTER * HIDDEN
+        tfs = flop / (ms["qqmm"] * 1e-3) / 1e12
+        out["qmm_tflops"] = round(tfs, 1)
+        out["roofline_qmm"] = {"bound": "mfma", "achieved": round(tfs, 1),
+                               "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                               "frac": round(tfs / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+                               "kernel": "NVFP4 qqmm M=2048 incl. activation quantize"}
+        for M in (1134, 4096):
+            key = f"qqmm_{M}"
+            if key in ms:
+                out[f"qmm_tflops_m{M}"] = round(2.0 * M * INTER * HIDDEN / (ms[key] * 1e-3) / 1e12, 1)
+    if "qmm_affine" in ms:
+        out["qmm_affine_tflops"] = round(2.0 * 2048 * INTER * HIDDEN / (ms["qmm_affine"] * 1e-3) / 1e12, 1)
+    if "qmm_mx" in ms:
+        out["qmm_mx_ms"] = stage_ms["qmm_mx"]
+    if "act_quant" in ms:
+        nbytes = 4096 * HIDDEN * 2 * 2 + 4096 * HIDDEN // 2 + 4096 * HIDDEN // 16
+        out["act_quant_gbs"] = round(nbytes / (ms["act_quant"] * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline and out["value"] is not None:
+        out["cpu_baseline"] = cpu_baseline(log)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(log):
+    """The oracle (plain C, fp64 matmul) on one affine W_up[25600,5120] qmv."""
+    import numpy as np
+
+    import synth_inputs as S
+    from oracle import oracle as o
+
+    x, w = S.affine_decode("up")
+    qo = o.quantize(o.AFFINE, w)
+    nbytes = affine_bytes(25600, 5120)
+    reps, t = 0, 0.0
+    while t < 10.0 and reps < 20:
+        t0 = time.perf_counter()
+        o.matmul_wonly(x, qo)
+        t += time.perf_counter() - t0
+        reps += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    gbs = nbytes * reps / t / 1e9
+    log(f"[bench] cpu oracle: {reps} affine qmv of [25600,5120] in {t:.1f}s -> {gbs:.3f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x affine g64 qmv W_up[25600,5120] (73.8 MB each), fp64 "
+                      "dequantize + fp64 dot products, OpenMP over outputs"}
+
+
+if __name__ == "__main__":
+    main()

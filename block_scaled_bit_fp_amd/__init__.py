@@ -1,0 +1,222 @@
+"""block_scaled_bit_fp_amd -- Python binding of libbsfp (MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libbsfp.so (see include/bsfp.h for the contract).  PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing, every call raises.
+
+    q = quantize(w_bf16, NVFP4)                 # QuantizedTensor on the GPU
+    y = qmv(x_bf16, q)                          # [M<=8, N] bf16 decode GEMV
+    y = qmm(x_bf16, q, act="same")              # [M, N] bf16 prefill GEMM
+    w_hat = dequantize(q)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsfp.so")
+
+AFFINE, MXFP4, NVFP4 = 0, 1, 2
+GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16}
+GS_NONE, GS_COMPUTE, GS_GIVEN = 0, 1, 2
+ACT_BF16, ACT_SAME = 0, 1
+STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
+
+EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
+           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_last_error", "bsfp_version")
+
+
+class QTensorDesc(C.Structure):
+    """Mirror of bsfp_qtensor."""
+    _fields_ = [("mode", C.c_int32), ("bits", C.c_int32), ("group_size", C.c_int32),
+                ("rows", C.c_int64), ("cols", C.c_int64),
+                ("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("global_scale", C.c_void_p), ("amax", C.c_void_p)]
+
+
+class BsfpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with block_scaled_bit_fp_amd/build.py "
+                "(there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        P, I64, I32 = C.c_void_p, C.c_int64, C.c_int32
+        QP = C.POINTER(QTensorDesc)
+        sigs = {
+            "bsfp_amax": (C.c_int, [P, I64, P, P]),
+            "bsfp_quantize": (C.c_int, [P, QP, I32, P]),
+            "bsfp_dequantize": (C.c_int, [QP, P, P]),
+            "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
+            "bsfp_qmm_workspace_bytes": (C.c_size_t, [I32, I64, I64, I32]),
+            "bsfp_qmm": (C.c_int, [P, I64, QP, I32, P, C.c_size_t, P, P]),
+            "bsfp_last_error": (C.c_char_p, []),
+            "bsfp_version": (C.c_char_p, []),
+        }
+        for name, (res, args) in sigs.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsfpError(status, lib().bsfp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def version() -> str:
+    return lib().bsfp_version().decode()
+
+
+@dataclass
+class QuantizedTensor:
+    """A quantized [rows, cols] tensor in device memory (see include/bsfp.h)."""
+    mode: int
+    rows: int
+    cols: int
+    codes: torch.Tensor                       # int32 [rows, cols/8] (uint32 words)
+    scales: torch.Tensor                      # uint8 [rows, cols/g] or bf16 (affine)
+    biases: Optional[torch.Tensor] = None     # bf16 [rows, cols/64] (affine)
+    global_scale: Optional[torch.Tensor] = None  # fp32 [1] (NVFP4 g)
+    amax: Optional[torch.Tensor] = None          # fp32 [1] (NVFP4 tensor amax)
+
+    @property
+    def group_size(self) -> int:
+        return GROUP[self.mode]
+
+    def desc(self) -> QTensorDesc:
+        return QTensorDesc(self.mode, 4, GROUP[self.mode], self.rows, self.cols,
+                           self.codes.data_ptr(), self.scales.data_ptr(),
+                           None if self.biases is None else self.biases.data_ptr(),
+                           None if self.global_scale is None else self.global_scale.data_ptr(),
+                           None if self.amax is None else self.amax.data_ptr())
+
+
+def empty_quantized(mode: int, rows: int, cols: int, device="cuda",
+                    global_scale: bool = True) -> QuantizedTensor:
+    G = GROUP[mode]
+    if cols % G:
+        raise ValueError(f"cols={cols} is not a multiple of the group size {G}")
+    codes = torch.empty((rows, cols // 8), dtype=torch.int32, device=device)
+    if mode == AFFINE:
+        scales = torch.empty((rows, cols // G), dtype=torch.bfloat16, device=device)
+        biases = torch.empty((rows, cols // G), dtype=torch.bfloat16, device=device)
+        return QuantizedTensor(mode, rows, cols, codes, scales, biases)
+    scales = torch.empty((rows, cols // G), dtype=torch.uint8, device=device)
+    gs = am = None
+    if mode == NVFP4 and global_scale:
+        gs = torch.empty(1, dtype=torch.float32, device=device)
+        am = torch.empty(1, dtype=torch.float32, device=device)
+    return QuantizedTensor(mode, rows, cols, codes, scales, None, gs, am)
+
+
+def _as_2d_bf16(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"expected bfloat16, got {x.dtype}")
+    if not x.is_cuda:
+        raise TypeError("expected a tensor on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return x.reshape(-1, x.shape[-1]) if x.dim() != 2 else x
+
+
+def amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |x| as a device fp32 [1] tensor."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("amax expects a contiguous bf16 GPU tensor")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().bsfp_amax(_ptr(x), x.numel(), _ptr(out), _stream()))
+    return out
+
+
+def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
+             g: Optional[torch.Tensor] = None,
+             out: Optional[QuantizedTensor] = None) -> QuantizedTensor:
+    """Quantize a bf16 [rows, cols] GPU tensor.  For NVFP4, global_scale is
+    'compute' (g = amax/2688), 'given' (use the fp32 [1] tensor g) or 'none'."""
+    x2 = _as_2d_bf16(x)
+    rows, cols = x2.shape
+    gs = {"none": GS_NONE, "compute": GS_COMPUTE, "given": GS_GIVEN}[global_scale]
+    if out is None:
+        out = empty_quantized(mode, rows, cols, x.device, global_scale=(gs != GS_NONE))
+        if mode == NVFP4 and gs == GS_GIVEN:
+            if g is None:
+                raise ValueError("global_scale='given' needs g")
+            out.global_scale.copy_(g.reshape(1).to(torch.float32))
+    if mode == NVFP4 and gs == GS_NONE:
+        out.global_scale = None
+    d = out.desc()
+    _check(lib().bsfp_quantize(_ptr(x2), C.byref(d), gs if mode == NVFP4 else 0, _stream()))
+    return out
+
+
+def dequantize(q: QuantizedTensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.codes.device)
+    d = q.desc()
+    _check(lib().bsfp_dequantize(C.byref(d), _ptr(out), _stream()))
+    return out
+
+
+def qmv(x: torch.Tensor, w: QuantizedTensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . dq(W)^T for M <= 8 (decode GEMV)."""
+    x2 = _as_2d_bf16(x)
+    M = x2.shape[0]
+    if x2.shape[1] != w.cols:
+        raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    if out is None:
+        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    d = w.desc()
+    _check(lib().bsfp_qmv(_ptr(x2), M, C.byref(d), _ptr(out), _stream()))
+    return out
+
+
+def qmm_workspace_bytes(mode: int, M: int, K: int, act: str = "bf16") -> int:
+    return int(lib().bsfp_qmm_workspace_bytes(mode, M, K, ACT_SAME if act == "same" else ACT_BF16))
+
+
+def qmm(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
+        workspace: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M, N] = x . dq(W)^T ('bf16') or alpha * dq0(q(x)) . dq0(W)^T ('same')."""
+    x2 = _as_2d_bf16(x)
+    M = x2.shape[0]
+    if x2.shape[1] != w.cols:
+        raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    a = ACT_SAME if act == "same" else ACT_BF16
+    need = int(lib().bsfp_qmm_workspace_bytes(w.mode, M, w.cols, a))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    d = w.desc()
+    _check(lib().bsfp_qmm(_ptr(x2), M, C.byref(d), a, _ptr(workspace),
+                          0 if workspace is None else workspace.numel(), _ptr(out), _stream()))
+    return out

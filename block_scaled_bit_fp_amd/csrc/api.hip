@@ -1,0 +1,217 @@
+// api.hip -- the C ABI of libbsfp (declared in include/bsfp.h).
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued, never throws, and reports failures as a status plus a
+// thread-local message (a C++ exception crossing a language bridge
+// terminates the process, and an unsupported group size that throws ends a
+// whole test binary: "feat(quant): backend quantization capability table and
+// load-time convert-or-reject policy", Gate impact).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "bsfp_internal.hpp"
+
+namespace bsfp {
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsfp_status fail(bsfp_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bsfp_status ok() {
+  g_err[0] = '\0';
+  return BSFP_OK;
+}
+
+bsfp_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSFP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int expected_group(int mode) {
+  switch (mode) {
+    case BSFP_AFFINE: return 64;
+    case BSFP_MXFP4: return 32;
+    case BSFP_NVFP4: return 16;
+    default: return -1;
+  }
+}
+
+const char* mode_name(int mode) {
+  switch (mode) {
+    case BSFP_AFFINE: return "affine";
+    case BSFP_MXFP4: return "mxfp4";
+    case BSFP_NVFP4: return "nvfp4";
+    default: return "unknown";
+  }
+}
+
+// Checks the descriptor of a quantized tensor; need_data: its code/scale
+// buffers must be present (non-empty tensors).
+bsfp_status check_qtensor(const bsfp_qtensor* q, const char* fn) {
+  if (!q) return fail(BSFP_ERR_ARG, "%s: null tensor descriptor", fn);
+  if (q->mode < BSFP_AFFINE || q->mode > BSFP_NVFP4 || q->bits != 4 ||
+      q->group_size != expected_group(q->mode))
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "%s: unsupported format (mode %d, bits %d, group %d); supported: "
+                "(affine, 4, 64), (mxfp4, 4, 32), (nvfp4, 4, 16)",
+                fn, (int)q->mode, (int)q->bits, (int)q->group_size);
+  if (q->rows < 0 || q->cols < 0)
+    return fail(BSFP_ERR_ARG, "%s: negative shape [%lld, %lld]", fn, (long long)q->rows,
+                (long long)q->cols);
+  if (q->cols % q->group_size)
+    return fail(BSFP_ERR_ARG, "%s: cols %lld is not a multiple of the %s group size %d", fn,
+                (long long)q->cols, mode_name(q->mode), (int)q->group_size);
+  if (q->rows > 0 && q->cols > 0) {
+    if (!q->codes || !q->scales)
+      return fail(BSFP_ERR_ARG, "%s: null codes or scales", fn);
+    if (!aligned16(q->codes))
+      return fail(BSFP_ERR_ARG, "%s: codes pointer is not 16-byte aligned", fn);
+    if (q->mode == BSFP_AFFINE && !q->biases)
+      return fail(BSFP_ERR_ARG, "%s: affine tensor without biases", fn);
+  }
+  return ok();
+}
+
+std::mutex g_cu_mutex;
+int g_cu_count[64] = {0};
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+}  // namespace bsfp
+
+using namespace bsfp;
+
+extern "C" {
+
+const char* bsfp_last_error(void) { return g_err; }
+
+const char* bsfp_version(void) { return "bsfp 0.1.0 (gfx950)"; }
+
+bsfp_status bsfp_amax(const uint16_t* x, int64_t n, float* amax_out, bsfp_stream stream) {
+  if (n < 0) return fail(BSFP_ERR_ARG, "bsfp_amax: negative n");
+  if (!amax_out) return fail(BSFP_ERR_ARG, "bsfp_amax: null output");
+  if (n > 0 && (!x || !aligned16(x)))
+    return fail(BSFP_ERR_ARG, "bsfp_amax: x is null or not 16-byte aligned");
+  return device_status(launch_amax(x, n, amax_out, (hipStream_t)stream), "bsfp_amax");
+}
+
+bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                          bsfp_stream stream) {
+  bsfp_status st = check_qtensor(q, "bsfp_quantize");
+  if (st != BSFP_OK) return st;
+  const int64_t n = q->rows * q->cols;
+  hipStream_t s = (hipStream_t)stream;
+  if (q->mode == BSFP_NVFP4) {
+    if (gs < BSFP_GS_NONE || gs > BSFP_GS_GIVEN)
+      return fail(BSFP_ERR_ARG, "bsfp_quantize: bad global-scale flag %d", (int)gs);
+    if (gs != BSFP_GS_NONE && !q->global_scale)
+      return fail(BSFP_ERR_ARG, "bsfp_quantize: nvfp4 global scale requested but global_scale is null");
+    if (gs == BSFP_GS_COMPUTE && !q->amax)
+      return fail(BSFP_ERR_ARG, "bsfp_quantize: BSFP_GS_COMPUTE needs an amax buffer");
+  }
+  if (n > 0 && (!x || !aligned16(x)))
+    return fail(BSFP_ERR_ARG, "bsfp_quantize: x is null or not 16-byte aligned");
+  const int64_t n_words = n / 8;
+  hipError_t e = hipSuccess;
+  switch (q->mode) {
+    case BSFP_NVFP4:
+      if (gs == BSFP_GS_COMPUTE) {
+        e = launch_amax(x, n, q->amax, s);
+        if (e == hipSuccess)
+          e = launch_quantize_nvfp4(x, n_words, q->codes, (uint8_t*)q->scales, q->amax, 1,
+                                    q->global_scale, s);
+      } else if (n_words > 0) {
+        e = launch_quantize_nvfp4(x, n_words, q->codes, (uint8_t*)q->scales,
+                                  gs == BSFP_GS_GIVEN ? q->global_scale : nullptr, 0, nullptr, s);
+      }
+      break;
+    case BSFP_MXFP4:
+      if (n_words > 0) e = launch_quantize_mxfp4(x, n_words, q->codes, (uint8_t*)q->scales, s);
+      break;
+    default:
+      if (n_words > 0)
+        e = launch_quantize_affine(x, n_words, q->codes, (uint16_t*)q->scales, q->biases, s);
+      break;
+  }
+  return device_status(e, "bsfp_quantize");
+}
+
+bsfp_status bsfp_dequantize(const bsfp_qtensor* q, uint16_t* out, bsfp_stream stream) {
+  bsfp_status st = check_qtensor(q, "bsfp_dequantize");
+  if (st != BSFP_OK) return st;
+  if (q->rows * q->cols > 0 && (!out || !aligned16(out)))
+    return fail(BSFP_ERR_ARG, "bsfp_dequantize: out is null or not 16-byte aligned");
+  return device_status(launch_dequantize(*q, out, (hipStream_t)stream), "bsfp_dequantize");
+}
+
+bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w, uint16_t* y,
+                     bsfp_stream stream) {
+  bsfp_status st = check_qtensor(w, "bsfp_qmv");
+  if (st != BSFP_OK) return st;
+  if (M < 1 || M > 8) return fail(BSFP_ERR_ARG, "bsfp_qmv: M = %lld outside 1..8", (long long)M);
+  if (w->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmv: K must be positive");
+  if (!x || !aligned16(x)) return fail(BSFP_ERR_ARG, "bsfp_qmv: x is null or not 16-byte aligned");
+  if (w->rows > 0 && !y) return fail(BSFP_ERR_ARG, "bsfp_qmv: null y");
+  return device_status(launch_qmv(x, (int)M, *w, y, (hipStream_t)stream), "bsfp_qmv");
+}
+
+size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act) {
+  if (mode < BSFP_AFFINE || mode > BSFP_NVFP4 || M < 0 || K < 0) return 0;
+  if (act != BSFP_ACT_BF16 && act != BSFP_ACT_SAME) return 0;
+  return qmm_workspace_bytes(mode, M, K, act);
+}
+
+bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_t act,
+                     void* workspace, size_t workspace_bytes, uint16_t* y, bsfp_stream stream) {
+  bsfp_status st = check_qtensor(w, "bsfp_qmm");
+  if (st != BSFP_OK) return st;
+  if (M < 0) return fail(BSFP_ERR_ARG, "bsfp_qmm: negative M");
+  if (act != BSFP_ACT_BF16 && act != BSFP_ACT_SAME)
+    return fail(BSFP_ERR_ARG, "bsfp_qmm: bad activation mode %d", (int)act);
+  if (M == 0 || w->rows == 0) return ok();
+  if (w->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmm: K must be positive");
+  if (!x || !aligned16(x)) return fail(BSFP_ERR_ARG, "bsfp_qmm: x is null or not 16-byte aligned");
+  if (!y || !aligned16(y)) return fail(BSFP_ERR_ARG, "bsfp_qmm: y is null or not 16-byte aligned");
+  if (w->cols % 64)
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld is not a multiple of 64",
+                (long long)w->cols);
+  if (act == BSFP_ACT_SAME && w->mode == BSFP_AFFINE)
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_qmm: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only");
+  if (M > (1 << 30) || w->rows > (1 << 30) || w->cols > (1 << 30))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: dimensions beyond 2^30");
+  const size_t need = qmm_workspace_bytes(w->mode, M, w->cols, act);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(BSFP_ERR_ARG, "bsfp_qmm: workspace needs %zu bytes (16-byte aligned), got %zu",
+                need, workspace_bytes);
+  return device_status(launch_qmm(x, M, *w, act, workspace, y, (hipStream_t)stream), "bsfp_qmm");
+}
+
+}  // extern "C"

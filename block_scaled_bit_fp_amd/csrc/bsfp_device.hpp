@@ -1,0 +1,144 @@
+// bsfp_device.hpp -- device-side building blocks shared by the gfx950 kernels:
+// bf16 / E4M3 / E2M1 codecs, wave reductions, vector types.
+//
+// Format rules implemented here (the library's contract, include/bsfp.h):
+//   E2M1: round to nearest even with saturation at 6, sign kept.  The gfx950
+//         converter v_cvt_scalef32_pk_fp4_f32 with a unit scale implements
+//         exactly this (checked over every non-NaN fp32 input); it is the
+//         hardware form of the cvt.rn.satfinite.e2m1x2.f32 conversion named
+//         in "perf(cuda): enable hardware NVFP4/MXFP4 conversion on Blackwell
+//         builds" (Problem / Background).
+//   E4M3: OCP E4M3FN, nearest even, values above 448 saturate to 448
+//         (F8E4M3_MAX, "mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfp {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3
+
+// Non-negative fp32 -> E4M3 code, nearest even, > 448 -> 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s <= 448.0f)) return 0x7Eu;
+  if (s < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (m = 8 is 2^-6)
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  uint32_t u = __float_as_uint(s);
+  uint32_t e = (u >> 23) - 120u;  // E4M3 biased exponent (bias 7)
+  uint32_t m = u & 0x7FFFFFu;
+  uint32_t r = m + 0x7FFFFu + ((m >> 20) & 1u);  // round 23 -> 3 mantissa bits
+  return (e << 3) + (r >> 20);  // a mantissa carry moves into the exponent
+}
+
+// E4M3 code (sign bit ignored, never NaN here) -> fp32, exact.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;   // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E8M0 code -> 2^(c-127) as fp32 (c = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_decode(uint32_t c) {
+  return c ? __uint_as_float(c << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------- E2M1
+
+// Two fp32 -> two E2M1 codes written into byte `SEL` of `old` (a -> low
+// nibble, b -> high nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Eight fp32 -> one packed word (element i -> nibble i).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
+  uint32_t w = 0;
+  w = e2m1_pack2<0>(w, v[0], v[1]);
+  w = e2m1_pack2<1>(w, v[2], v[3]);
+  w = e2m1_pack2<2>(w, v[4], v[5]);
+  w = e2m1_pack2<3>(w, v[6], v[7]);
+  return w;
+}
+
+// Byte `SEL` of w (two codes) -> two bf16 values (low nibble -> .x), exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Byte `SEL` of w (two codes) -> two fp16 values (low nibble -> .x), exact.
+template <int SEL>
+__device__ __forceinline__ f16x2_t e2m1x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Byte `SEL` of w -> two fp32 values, exact.
+template <int SEL>
+__device__ __forceinline__ f32x2_t e2m1x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Bytes (2*HI, 2*HI+1) of w, each holding a value 0..15, -> the two integers
+// as bf16 (exact).  An OCP E4M3 byte 0..15 decodes to code * 2^-9 (subnormals
+// and the first normal binade), and the converter's unit-exponent scale 2^9
+// restores the integer.
+template <bool HI>
+__device__ __forceinline__ uint32_t nibbles_to_bf16x2(uint32_t w) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------- dot
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs, fp32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------- reductions
+
+// Butterfly over lanes differing in the bits of MASK..1 (power-of-two team).
+template <int WIDTH>
+__device__ __forceinline__ float team_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float team_min(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float team_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace bsfp

@@ -1,0 +1,47 @@
+// bsfp_internal.hpp -- launchers shared between the translation units of
+// libbsfp.  Every launcher enqueues on `s`, assumes its arguments were
+// validated by the C-ABI layer (api.hip) and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bsfp.h"
+
+namespace bsfp {
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---- amax / quantize / dequantize (quantize.hip)
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_t s);
+
+// NVFP4 quantize.  g_src: NULL (no global scale, g = 1), or a device fp32
+// holding g (g_src_is_amax == 0) or the tensor amax (g_src_is_amax == 1, g =
+// amax/2688).  g_out (may be NULL) receives the g used.
+hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                 uint8_t* scales, const float* g_src, int g_src_is_amax,
+                                 float* g_out, hipStream_t s);
+// NVFP4 quantize + dequantize without the global scale into fp16 xhat
+// [n_words * 8] (the qq GEMM's activation operand).
+hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words, void* xhat,
+                                             const float* g_src, int g_src_is_amax,
+                                             float* g_out, hipStream_t s);
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                  uint16_t* scales, uint16_t* biases, hipStream_t s);
+
+hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s);
+
+// ---- qmv (qmv.hip)
+hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
+                      hipStream_t s);
+
+// ---- qmm (qmm.hip)
+size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act);
+hipError_t launch_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor& w, int act,
+                      void* ws, uint16_t* y, hipStream_t s);
+
+}  // namespace bsfp

@@ -1,0 +1,407 @@
+// qmm.hip -- prefill GEMM y[M, N] = x[M, K] . W[N, K]^T on MFMA for gfx950.
+//
+// Two kernels share one tiling scheme (4 waves in a 2 x 2 arrangement, each
+// wave owning WMT x WNT tiles of 32 x 32 outputs, K advanced 64 at a time):
+//
+// gemm_dq_kernel -- 16-bit MFMA (v_mfma_f32_32x32x16_{bf16,f16}) with the
+//   weights dequantized in registers.  The 16-bit A operand (bf16 x, or the
+//   fp16 dequantized NVFP4 activations of the qq path) is staged through LDS
+//   (double-buffered, XOR-swizzled 16-byte chunks so the 32 rows a wave reads
+//   at one k offset fall in different banks).  The packed weight codes never
+//   touch LDS: each lane loads the 16-byte code chunk (32 k-values) of its
+//   own weight row one K-step ahead and expands it right before the MFMA.
+//   The contraction order inside a 64-wide K step is permuted consistently
+//   for both operands: at MFMA step kk, lane half h covers k = 32h + 8kk ..
+//   32h + 8kk + 7, so that each lane reads whole code words.
+//     NVFP4 qq (fp16): E2M1 * E4M3 is exact in fp16, so the weight expands
+//       with one v_cvt_scalef32_pk_f16_fp4 and one v_pk_mul_f16 per pair.
+//     NVFP4 weight-only (bf16): E2M1 -> fp32 pair, times the block scale,
+//       packed to bf16 (exact).
+//     MXFP4 weight-only (bf16): v_cvt_scalef32_pk_bf16_fp4 with the E8M0
+//       block scale as the converter's exponent scale (exact).
+//     affine weight-only (bf16): s * q + b rounded once to bf16 (the
+//       "dequantize to bf16, then a bf16 GEMM" numerics of "mlx: opt-in dense
+//       GEMM for nvfp4 prefill"); q comes from the exact fp8-byte decode.
+//   The per-tensor scale (g_w, or alpha = g_x * g_w for qq) is applied in the
+//   epilogue ("mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu: alpha =
+//   amax_x * amax_w / (448*6)^2, read on the device).
+//
+// gemm_mx_kernel -- MXFP4 x MXFP4 on the CDNA4 block-scaled MFMA
+//   v_mfma_scale_f32_32x32x64_f8f6f4: both operands stay 4-bit, and each
+//   lane hands the MFMA the E8M0 scale of the 32 k-values it holds, which is
+//   exactly one MXFP4 group.  No dequantization at all.
+//
+// fp32 accumulation, bf16 round-to-nearest-even output, rows and columns
+// beyond M / N clamped on load and masked on store.
+#include "bsfp_device.hpp"
+#include "bsfp_internal.hpp"
+
+namespace bsfp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+enum { DEC_AFFINE = 0, DEC_MXFP4 = 1, DEC_NVFP4 = 2, DEC_NVFP4_F16 = 3 };
+
+// Expanded B operand of one MFMA (8 consecutive k of one weight row).
+struct Op8 {
+  uint32_t v[4];
+};
+
+// Per-lane per-K-step weight data of one 32-column subtile.
+struct BFrag {
+  uint4 codes;   // 32 codes: k = k0 + 32h + 0..31
+  uint32_t s0;   // scale bits (mode specific)
+  uint32_t s1;   // affine bias bits
+};
+
+template <int DEC>
+__device__ __forceinline__ void load_bfrag(BFrag& f, const uint32_t* __restrict__ codes,
+                                           const void* __restrict__ scales,
+                                           const uint16_t* __restrict__ biases, int64_t n,
+                                           int K, int k0, int h) {
+  f.codes = *reinterpret_cast<const uint4*>(codes + n * (K / 8) + (k0 / 8) + 4 * h);
+  if constexpr (DEC == DEC_AFFINE) {
+    const int64_t gi = n * (K / 64) + k0 / 64;
+    f.s0 = reinterpret_cast<const uint16_t*>(scales)[gi];
+    f.s1 = biases[gi];
+  } else if constexpr (DEC == DEC_MXFP4) {
+    f.s0 = reinterpret_cast<const uint8_t*>(scales)[n * (K / 32) + k0 / 32 + h];
+  } else {  // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
+    f.s0 = reinterpret_cast<const uint16_t*>(scales)[n * (K / 32) + k0 / 32 + h];
+  }
+}
+
+// Expand word kk of the fragment (k = 32h + 8kk + 0..7).
+template <int DEC>
+__device__ __forceinline__ Op8 expand(const BFrag& f, int kk) {
+  const uint32_t w = kk == 0 ? f.codes.x : kk == 1 ? f.codes.y : kk == 2 ? f.codes.z : f.codes.w;
+  Op8 o;
+  if constexpr (DEC == DEC_NVFP4_F16) {
+    const uint32_t sb = (kk < 2) ? (f.s0 & 0xFFu) : (f.s0 >> 8);
+    const _Float16 sh = (_Float16)e4m3_decode(sb);
+    const f16x2_t s2 = {sh, sh};
+    o.v[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
+    o.v[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
+    o.v[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
+    o.v[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
+  } else if constexpr (DEC == DEC_NVFP4) {
+    const uint32_t sb = (kk < 2) ? (f.s0 & 0xFFu) : (f.s0 >> 8);
+    const float sc = e4m3_decode(sb);
+    f32x2_t p0 = e2m1x2_to_f32x2<0>(w), p1 = e2m1x2_to_f32x2<1>(w);
+    f32x2_t p2 = e2m1x2_to_f32x2<2>(w), p3 = e2m1x2_to_f32x2<3>(w);
+    o.v[0] = pack_bf16x2(p0.x * sc, p0.y * sc);
+    o.v[1] = pack_bf16x2(p1.x * sc, p1.y * sc);
+    o.v[2] = pack_bf16x2(p2.x * sc, p2.y * sc);
+    o.v[3] = pack_bf16x2(p3.x * sc, p3.y * sc);
+  } else if constexpr (DEC == DEC_MXFP4) {
+    const float sc = __uint_as_float(f.s0 << 23);  // the converter reads its exponent only
+    o.v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    o.v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    o.v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    o.v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  } else {  // affine: s * q + b, one rounding to bf16
+    const float s = __uint_as_float(f.s0 << 16), b = __uint_as_float(f.s1 << 16);
+    const uint32_t t = w & 0x0F0F0F0Fu, u = (w >> 4) & 0x0F0F0F0Fu;
+    // t holds q0, q2, q4, q6 in its bytes; u holds q1, q3, q5, q7
+    const f32x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, false);  // q0, q2
+    const f32x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, true);   // q4, q6
+    const f32x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, false);  // q1, q3
+    const f32x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, true);   // q5, q7
+    o.v[0] = pack_bf16x2(__builtin_fmaf(s, a0.x, b), __builtin_fmaf(s, b0.x, b));
+    o.v[1] = pack_bf16x2(__builtin_fmaf(s, a0.y, b), __builtin_fmaf(s, b0.y, b));
+    o.v[2] = pack_bf16x2(__builtin_fmaf(s, a1.x, b), __builtin_fmaf(s, b1.x, b));
+    o.v[3] = pack_bf16x2(__builtin_fmaf(s, a1.y, b), __builtin_fmaf(s, b1.y, b));
+  }
+  return o;
+}
+
+template <int DEC>
+__device__ __forceinline__ f32x16_t mfma16(const uint4& a, const Op8& b, const f32x16_t& c) {
+  const uint4 bv = {b.v[0], b.v[1], b.v[2], b.v[3]};
+  if constexpr (DEC == DEC_NVFP4_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+  }
+}
+
+// XCD-aware tile order: workgroup b runs on XCD b % 8, so consecutive logical
+// tiles (which share a weight column block across the M tiles) are given to
+// workgroups of one XCD and hit the same L2.
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {
+  int b = blockIdx.x;
+  const int T = tiles_m * tiles_n;
+  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+  tm = b % tiles_m;
+  tn = b / tiles_m;
+}
+
+template <int DEC, int WMT, int WNT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dq_kernel(
+    const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
+    const void* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const float* __restrict__ g1, const float* __restrict__ g2, int M, int N, int K,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+  constexpr int BM = 64 * WMT;
+  constexpr int ACH = BM / 32;  // 16-byte A chunks per thread per K step
+  extern __shared__ uint4 lds[];  // [2][BM][8] chunks, XOR-swizzled
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m_base = tm * BM, n_base = tn * (64 * WNT);
+
+  uint4 areg[ACH];
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+      const int q = tid + kThreads * c, r = q >> 3, ch = q & 7;
+      const int gm = min(m_base + r, M - 1);
+      areg[c] = *reinterpret_cast<const uint4*>(A + (int64_t)gm * K + k0 + ch * 8);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+      const int q = tid + kThreads * c, r = q >> 3, ch = q & 7;
+      lds[(buf * BM + r) * 8 + (ch ^ (r & 7))] = areg[c];
+    }
+  };
+
+  int64_t nrow[WNT];
+#pragma unroll
+  for (int j = 0; j < WNT; ++j) nrow[j] = min(n_base + wn * 32 * WNT + 32 * j + l32, N - 1);
+  BFrag bnext[WNT];
+  auto load_b = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) load_bfrag<DEC>(bnext[j], codes, scales, biases, nrow[j], K, k0, h);
+  };
+
+  f32x16_t acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  __syncthreads();
+
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int buf = (k0 >> 6) & 1;
+    BFrag bcur[WNT];
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) bcur[j] = bnext[j];
+    const bool more = k0 + 64 < K;
+    if (more) {
+      load_a(k0 + 64);
+      load_b(k0 + 64);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 a[WMT];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int r = wm * 32 * WMT + 32 * i + l32;
+        a[i] = lds[(buf * BM + r) * 8 + ((4 * h + kk) ^ (r & 7))];
+      }
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const Op8 b = expand<DEC>(bcur[j], kk);
+#pragma unroll
+        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], b, acc[i][j]);
+      }
+    }
+    if (more) store_a(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int n = n_base + wn * 32 * WNT + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m_base + wm * 32 * WMT + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+      }
+    }
+}
+
+// MXFP4 x MXFP4 on the block-scaled MFMA.  Operands come straight from the
+// packed codes in global memory (L2-resident across the tiles that share
+// them), one K step (64) ahead.
+template <int WMT, int WNT>
+__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
+    const uint32_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+    const uint32_t* __restrict__ wc, const uint8_t* __restrict__ wsc, int M, int N, int K,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * 64 * WMT + wm * 32 * WMT, n0 = tn * 64 * WNT + wn * 32 * WNT;
+
+  int64_t mr[WMT], nr[WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i) mr[i] = min(m0 + 32 * i + l32, M - 1);
+#pragma unroll
+  for (int j = 0; j < WNT; ++j) nr[j] = min(n0 + 32 * j + l32, N - 1);
+
+  uint4 an[WMT], bn[WNT];
+  uint32_t asn[WMT], bsn[WNT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      an[i] = *reinterpret_cast<const uint4*>(xc + mr[i] * (K / 8) + k0 / 8 + 4 * h);
+      asn[i] = xs[mr[i] * (K / 32) + k0 / 32 + h];
+    }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      bn[j] = *reinterpret_cast<const uint4*>(wc + nr[j] * (K / 8) + k0 / 8 + 4 * h);
+      bsn[j] = wsc[nr[j] * (K / 32) + k0 / 32 + h];
+    }
+  };
+
+  f32x16_t acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    uint4 ac[WMT], bc[WNT];
+    uint32_t asc[WMT], bsc[WNT];
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) { ac[i] = an[i]; asc[i] = asn[i]; }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) { bc[j] = bn[j]; bsc[j] = bsn[j]; }
+    if (k0 + 64 < K) load(k0 + 64);
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      const i32x8_t av = {(int)ac[i].x, (int)ac[i].y, (int)ac[i].z, (int)ac[i].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const i32x8_t bv = {(int)bc[j].x, (int)bc[j].y, (int)bc[j].z, (int)bc[j].w, 0, 0, 0, 0};
+        // formats 4/4: FP4 E2M1 for both operands; scales: E8M0 byte 0
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            av, bv, acc[i][j], 4, 4, 0, (int)asc[i], 0, (int)bsc[j]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int n = n0 + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+      }
+    }
+}
+
+template <int DEC, int WMT>
+hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
+                  const float* g2, uint16_t* y, hipStream_t s) {
+  constexpr int WNT = 4;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
+  const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
+  const size_t lds = (size_t)2 * 64 * WMT * 8 * sizeof(uint4);
+  hipLaunchKernelGGL((gemm_dq_kernel<DEC, WMT, WNT>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                     lds, s, A, w.codes, w.scales, w.biases, g1, g2, M, N, K, y, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+template <int DEC>
+hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
+                    const float* g2, uint16_t* y, hipStream_t s) {
+  if (M <= 64) return run_dq<DEC, 1>(A, M, w, g1, g2, y, s);
+  if (M <= 128) return run_dq<DEC, 2>(A, M, w, g1, g2, y, s);
+  return run_dq<DEC, 4>(A, M, w, g1, g2, y, s);
+}
+
+hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,
+                  uint16_t* y, hipStream_t s) {
+  constexpr int WMT = 1, WNT = 1;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
+  const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
+  hipLaunchKernelGGL((gemm_mx_kernel<WMT, WNT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
+                     xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// Workspace for the qq paths:
+//   NVFP4: [amax f32, g_x f32] (256 B) + xhat fp16 [M, K]
+//   MXFP4: x codes uint32 [M, K/8] + x scales uint8 [M, K/32]
+size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act) {
+  if (act != BSFP_ACT_SAME) return 0;
+  if (mode == BSFP_NVFP4) return 256 + align256((size_t)M * K * 2);
+  if (mode == BSFP_MXFP4) return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+  return 0;
+}
+
+hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int act, void* ws,
+                      uint16_t* y, hipStream_t s) {
+  const int M = (int)M64;
+  if (act == BSFP_ACT_BF16) {
+    switch (w.mode) {
+      case BSFP_AFFINE: return run_dq_m<DEC_AFFINE>(x, M, w, nullptr, nullptr, y, s);
+      case BSFP_MXFP4: return run_dq_m<DEC_MXFP4>(x, M, w, nullptr, nullptr, y, s);
+      default: return run_dq_m<DEC_NVFP4>(x, M, w, w.global_scale, nullptr, y, s);
+    }
+  }
+  const int64_t n = M64 * w.cols;
+  if (w.mode == BSFP_NVFP4) {
+    float* amax = reinterpret_cast<float*>(ws);
+    float* gx = amax + 1;
+    uint16_t* xhat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + 256);
+    hipError_t e = hipSuccess;
+    if (w.global_scale) {  // alpha = g_x * g_w with g_x = amax_x / 2688
+      e = launch_amax(x, n, amax, s);
+      if (e == hipSuccess) e = launch_quantize_dequant_nvfp4_f16(x, n / 8, xhat, amax, 1, gx, s);
+      if (e != hipSuccess) return e;
+      return run_dq_m<DEC_NVFP4_F16>(xhat, M, w, gx, w.global_scale, y, s);
+    }
+    e = launch_quantize_dequant_nvfp4_f16(x, n / 8, xhat, nullptr, 0, nullptr, s);
+    if (e != hipSuccess) return e;
+    return run_dq_m<DEC_NVFP4_F16>(xhat, M, w, nullptr, nullptr, y, s);
+  }
+  // MXFP4
+  uint32_t* xc = reinterpret_cast<uint32_t*>(ws);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws) + align256((size_t)n / 2);
+  hipError_t e = launch_quantize_mxfp4(x, n / 8, xc, xs, s);
+  if (e != hipSuccess) return e;
+  return run_mx(xc, xs, M, w, y, s);
+}
+
+}  // namespace bsfp

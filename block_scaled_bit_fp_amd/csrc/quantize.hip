@@ -1,0 +1,339 @@
+// quantize.hip -- tensor amax, quantize (NVFP4 / MXFP4 / affine 4-bit) and
+// dequantize kernels for gfx950.
+//
+// All three quantizers are HBM-bound streaming kernels over the flattened
+// tensor: one lane owns 8 consecutive elements (one 16-byte load, one packed
+// output word), a group is a power-of-two team of adjacent lanes (NVFP4 16
+// elements = 2 lanes, MXFP4 32 = 4, affine 64 = 8), and the group statistic
+// is a butterfly over the team.  Because cols is a multiple of the group
+// size, groups never straddle rows, so the flat word index maps directly to
+// the row-major code, scale and bias arrays.
+//
+// This file is compiled with -ffp-contract=off: every fp32 operation below is
+// one correctly rounded IEEE operation, which keeps codes and scales
+// bit-identical to the documented rules.
+//
+// Rules (the pages give the interfaces, not the arithmetic; the steps below
+// are the library's contract, include/bsfp.h):
+//   NVFP4  g = amax/2688 (448*6; "mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu);
+//          S = E4M3(bamax / (6g)); d = E4M3(S)*g; code = E2M1(x * (1/d)),
+//          d == 0 -> scale 0 and codes 0.
+//   MXFP4  e = floor(log2 bamax) - 2 clamped to [-127, 127] (OCP MX shared
+//          exponent); S = e + 127; code = E2M1(x * 2^-e).
+//   AFFINE s = bf16((max - min)/15), b = bf16(min) = min,
+//          q = clamp(rint((x - b) * (1/s)), 0, 15), s == 0 -> q = 0.
+#include "bsfp_device.hpp"
+#include "bsfp_internal.hpp"
+
+namespace bsfp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// ------------------------------------------------------------------ amax
+
+__global__ void amax_init_kernel(float* out) { *out = 0.0f; }
+
+// max |x| over n bf16 values.  Non-negative fp32 values order like their
+// bit patterns, so the cross-workgroup step is an integer atomic max.
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ x,
+                                                         int64_t n, float* __restrict__ out) {
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nv = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
+    uint4 v = xv[i];
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+  }
+  if (blockIdx.x == 0) {  // the n % 8 tail
+    int64_t t = (nv << 3) + threadIdx.x;
+    if (t < n) m = fmaxf(m, fabsf(bf16_to_f32(x[t])));
+  }
+  m = team_max<64>(m);
+  __shared__ float part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = part[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, part[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(r));
+  }
+}
+
+// ------------------------------------------------------------------ NVFP4
+
+__global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
+    const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, const float* __restrict__ g_src, int g_src_is_amax,
+    float* __restrict__ g_out) {
+  float g = 1.0f;
+  if (g_src) g = g_src_is_amax ? (*g_src / 2688.0f) : *g_src;
+  if (g_out && blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
+  const float six_g = 6.0f * g;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // even: lane pairs stay together
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = team_max<2>(a);  // 16-element group = lanes (2j, 2j+1)
+    uint32_t S = 0;
+    float d = 0.0f;
+    if (g != 0.0f) {
+      float sf = a / six_g;
+      S = e4m3_encode(sf);
+      d = e4m3_decode(S) * g;
+    }
+    uint32_t w = 0;
+    if (d != 0.0f) {
+      const float inv = 1.0f / d;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
+      w = e2m1_pack8(v);
+    } else {
+      S = 0;
+    }
+    codes[i] = w;
+    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)S;
+  }
+}
+
+// NVFP4 quantize immediately followed by dequantization without the global
+// scale: xhat = E2M1(code) * E4M3(S), written as fp16 (exact: at most 6
+// significant bits, magnitudes 2^-10 .. 2688).  This is the activation
+// operand of the NVFP4 qq GEMM (the pages' fp_quantize_dequantize, "mlx
+// 0.30.7.3 -> 0.30.7.6", qqmm.cpp); the codes and scales are those
+// bsfp_quantize produces for the same input and global scale.
+__global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_f16_kernel(
+    const uint4* __restrict__ x, int64_t n_words, uint4* __restrict__ xhat,
+    const float* __restrict__ g_src, int g_src_is_amax, float* __restrict__ g_out) {
+  float g = 1.0f;
+  if (g_src) g = g_src_is_amax ? (*g_src / 2688.0f) : *g_src;
+  if (g_out && blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
+  const float six_g = 6.0f * g;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = team_max<2>(a);
+    uint32_t S = 0;
+    float d = 0.0f;
+    if (g != 0.0f) {
+      S = e4m3_encode(a / six_g);
+      d = e4m3_decode(S) * g;
+    }
+    uint4 o = {0u, 0u, 0u, 0u};
+    if (d != 0.0f) {
+      const float inv = 1.0f / d;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
+      const uint32_t w = e2m1_pack8(v);
+      const _Float16 sh = (_Float16)e4m3_decode(S);  // exact in fp16
+      const f16x2_t s2 = {sh, sh};
+      o.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
+      o.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
+      o.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
+      o.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
+    }
+    xhat[i] = o;
+  }
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+__global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
+    const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = team_max<4>(a);  // 32-element group = 4 lanes
+    // floor(log2 a) = biased exponent - 127 for normal a; subnormal or zero
+    // a gives an exponent below -128, which the clamp maps to -127.
+    const int be = (int)(__float_as_uint(a) >> 23);
+    const int e = max(be - 129, -127);  // e <= 125 for finite bf16 input
+    const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
+    codes[i] = e2m1_pack8(v);
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+  }
+}
+
+// ------------------------------------------------------------------ affine
+
+__global__ __launch_bounds__(kThreads) void quantize_affine_kernel(
+    const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ biases) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 8
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float mn = f[0], mx = f[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) { mn = fminf(mn, f[k]); mx = fmaxf(mx, f[k]); }
+    mn = team_min<8>(mn);  // 64-element group = 8 lanes
+    mx = team_max<8>(mx);
+    const float step = (mx - mn) / 15.0f;
+    const uint32_t sb = f32_to_bf16(step);
+    const uint32_t bb = __float_as_uint(mn) >> 16;  // mn is a bf16 value: exact
+    const float sc = __uint_as_float(sb << 16);
+    const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float q = __builtin_rintf((f[k] - mn) * inv);
+      q = fminf(fmaxf(q, 0.0f), 15.0f);
+      w |= (uint32_t)q << (4 * k);
+    }
+    codes[i] = w;
+    if ((i & 7) == 0) {
+      scales[i >> 3] = (uint16_t)sb;
+      biases[i >> 3] = (uint16_t)bb;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dequantize
+
+// One lane per packed word: 8 codes -> 8 bf16 (one 16-byte store).
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+    const uint32_t* __restrict__ codes, const void* __restrict__ scales,
+    const uint16_t* __restrict__ biases, const float* __restrict__ gptr, int64_t n_words,
+    uint4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const float g = gptr ? *gptr : 1.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    const uint32_t w = codes[i];
+    float v[8];
+    if constexpr (MODE == BSFP_AFFINE) {
+      const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[i >> 3]);
+      const float b = bf16_to_f32(biases[i >> 3]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(s, (float)((w >> (4 * k)) & 15u), b);
+    } else {
+      f32x2_t p0 = e2m1x2_to_f32x2<0>(w), p1 = e2m1x2_to_f32x2<1>(w);
+      f32x2_t p2 = e2m1x2_to_f32x2<2>(w), p3 = e2m1x2_to_f32x2<3>(w);
+      v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+      v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+      const uint8_t* s8 = reinterpret_cast<const uint8_t*>(scales);
+      if constexpr (MODE == BSFP_NVFP4) {
+        const float sc = e4m3_decode(s8[i >> 1]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (v[k] * sc) * g;  // product exact, then one rounding
+      } else {
+        const float sc = e8m0_decode(s8[i >> 2]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = v[k] * sc;  // exact power-of-two scaling
+      }
+    }
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    out[i] = o;
+  }
+}
+
+// Grid for a flat streaming kernel: enough workgroups to fill every CU
+// several times over, no more than the work needs.
+int stream_grid(int64_t items) {
+  const int64_t want = (items + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * 32;
+  return (int)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_t s) {
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax_out);
+  if (n > 0) {
+    const int64_t nv = n >> 3;
+    int grid = stream_grid(nv);
+    if (grid > device_cu_count() * 8) grid = device_cu_count() * 8;
+    hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kThreads), 0, s, x, n, amax_out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                 uint8_t* scales, const float* g_src, int g_src_is_amax,
+                                 float* g_out, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint4*>(x), n_words, codes, scales, g_src,
+                     g_src_is_amax, g_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words, void* xhat,
+                                             const float* g_src, int g_src_is_amax,
+                                             float* g_out, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_dequant_nvfp4_f16_kernel, dim3(stream_grid(n_words)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
+                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                 uint8_t* scales, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint4*>(x), n_words, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* codes,
+                                  uint16_t* scales, uint16_t* biases, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_affine_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint4*>(x), n_words, codes, scales, biases);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s) {
+  const int64_t n_words = q.rows * q.cols / 8;
+  if (n_words == 0) return hipGetLastError();
+  const dim3 grid(stream_grid(n_words)), block(kThreads);
+  uint4* o = reinterpret_cast<uint4*>(out);
+  switch (q.mode) {
+    case BSFP_AFFINE:
+      hipLaunchKernelGGL(dequantize_kernel<BSFP_AFFINE>, grid, block, 0, s, q.codes, q.scales,
+                         q.biases, nullptr, n_words, o);
+      break;
+    case BSFP_MXFP4:
+      hipLaunchKernelGGL(dequantize_kernel<BSFP_MXFP4>, grid, block, 0, s, q.codes, q.scales,
+                         nullptr, nullptr, n_words, o);
+      break;
+    default:
+      hipLaunchKernelGGL(dequantize_kernel<BSFP_NVFP4>, grid, block, 0, s, q.codes, q.scales,
+                         nullptr, q.global_scale, n_words, o);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsfp

@@ -1,0 +1,183 @@
+/*
+ * bsfp.h -- C ABI of libbsfp: block-scaled 4-bit quantization and quantized
+ * matmul on AMD Instinct MI355X (gfx950).
+ *
+ * Formats (the contract; element k of a row is nibble k%8 of uint32 word k/8,
+ * low nibble first; every tensor row-major and contiguous):
+ *
+ *   BSFP_NVFP4  bits 4, group 16.  codes: E2M1 (FP4) packed 8 per uint32.
+ *               scales: uint8 E4M3 (OCP E4M3FN) per 16-element group.
+ *               global_scale: optional fp32 g = amax/(448*6) per tensor.
+ *               Value = E2M1(c) * E4M3(S) * g.
+ *               (native NVFP4 is group 16 / bits 4: "feat(quant): backend
+ *               quantization capability table ...", Gate impact; 448 and 6
+ *               are F8E4M3_MAX and F4E2M1_MAX in "mlx 0.30.7.3 -> 0.30.7.6",
+ *               qqmm_utils.cu.)
+ *   BSFP_MXFP4  bits 4, group 32.  codes: E2M1.  scales: uint8 E8M0
+ *               (2^(S-127)).  Value = E2M1(c) * 2^(S-127).
+ *               (MX scale arm of the bits == 4 quantizer: "perf(cuda): enable
+ *               hardware NVFP4/MXFP4 conversion on Blackwell builds",
+ *               Current Behavior.)
+ *   BSFP_AFFINE bits 4, group 64.  codes: unsigned 0..15.  scales, biases:
+ *               bf16 per group.  Value = s*q + b.
+ *               (affine 4-bit / group 64: "epic: NVIDIA Volta (sm_70)
+ *               inference acceleration program", Baseline.)
+ *
+ *   Codes and scales are uint32 [rows, cols/8] and [rows, cols/group]; the
+ *   packed shape follows quantize_input in "mlx 0.30.7.3 -> 0.30.7.6"
+ *   (qqmm.cpp): last dim = cols*bits/32.  Scales are linear (not the tiled
+ *   layout that file builds for cuBLASLt).
+ *
+ * Quantization rounds to nearest even and saturates (cvt.rn.satfinite.
+ * e2m1x2.f32 in "perf(cuda): enable hardware NVFP4/MXFP4 conversion on
+ * Blackwell builds", Problem / Background).  Block scales:
+ *   NVFP4  S = E4M3(bamax / (6*g)), codes = E2M1(x * (1 / (E4M3(S)*g)))
+ *   MXFP4  e = floor(log2 bamax) - 2, codes = E2M1(x * 2^-e), S = e + 127
+ *   AFFINE s = bf16((max-min)/15), b = bf16(min), q = rint((x-b)/s) in 0..15
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers of the current HIP device, 16-byte
+ *     aligned; bf16 travels as uint16 bit patterns.  The caller owns and
+ *     allocates every buffer (the library allocates no device memory, never
+ *     frees, and never writes its inputs).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     with no host synchronization.
+ *   - Functions never throw and never abort.  Argument errors are detected on
+ *     the host before anything is enqueued and return BSFP_ERR_ARG; a
+ *     format outside the three above returns BSFP_ERR_UNSUPPORTED; a failed
+ *     launch returns BSFP_ERR_DEVICE.  bsfp_last_error() then describes it.
+ *     (A C++ exception crossing a language bridge terminates the process, and
+ *     an unsupported group size that throws aborts a whole test binary:
+ *     "feat(quant): backend quantization capability table ...", Gate impact.)
+ */
+#ifndef BSFP_H
+#define BSFP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BSFP_AFFINE = 0, BSFP_MXFP4 = 1, BSFP_NVFP4 = 2 } bsfp_mode;
+
+typedef enum {
+    BSFP_OK = 0,
+    BSFP_ERR_ARG = 1,          /* bad pointer, size, alignment or shape */
+    BSFP_ERR_UNSUPPORTED = 2,  /* (mode, bits, group) outside the contract */
+    BSFP_ERR_DEVICE = 3        /* launch failure reported by the runtime */
+} bsfp_status;
+
+/* Activation handling of bsfp_qmm. */
+typedef enum {
+    BSFP_ACT_BF16 = 0,  /* weight-only: y = x . dq(W)^T, x stays bf16 */
+    BSFP_ACT_SAME = 1   /* qq: x is quantized with W's mode first, then
+                           y = alpha * dq0(q(x)) . dq0(W)^T */
+} bsfp_act;
+
+/* NVFP4 global-scale handling of bsfp_quantize. */
+typedef enum {
+    BSFP_GS_NONE = 0,     /* no global scale: g = 1 */
+    BSFP_GS_COMPUTE = 1,  /* amax over the tensor -> *amax, g = amax/2688 ->
+                             *global_scale (both must be non-NULL) */
+    BSFP_GS_GIVEN = 2     /* use the device fp32 *global_scale as g */
+} bsfp_gs;
+
+typedef void* bsfp_stream; /* hipStream_t */
+
+/* A quantized tensor: logical bf16 shape [rows, cols]. */
+typedef struct {
+    int32_t mode;          /* bsfp_mode */
+    int32_t bits;          /* 4 */
+    int32_t group_size;    /* 16 NVFP4, 32 MXFP4, 64 AFFINE */
+    int64_t rows, cols;    /* cols % group_size == 0 */
+    uint32_t* codes;       /* [rows, cols/8] */
+    void* scales;          /* NVFP4/MXFP4 uint8, AFFINE bf16: [rows, cols/group] */
+    uint16_t* biases;      /* AFFINE bf16 [rows, cols/group]; NULL otherwise */
+    float* global_scale;   /* NVFP4 g (device fp32) or NULL for none */
+    float* amax;           /* NVFP4 tensor amax (device fp32), written by
+                              BSFP_GS_COMPUTE; may be NULL otherwise */
+} bsfp_qtensor;
+
+/*
+ * bsfp_amax: *amax_out = max |x_i| over the n bf16 values at x (device
+ * fp32).  The source of the NVFP4 global scale (alpha = amax_x*amax_w /
+ * (448*6)^2: "mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu,
+ * compute_qqmm_pointers).  n >= 0 (n == 0 gives 0).  Exact and independent
+ * of reduction order.
+ */
+bsfp_status bsfp_amax(const uint16_t* x, int64_t n, float* amax_out,
+                      bsfp_stream stream);
+
+/*
+ * bsfp_quantize: bf16 x [q->rows, q->cols] -> q->codes, q->scales (and
+ * q->biases for AFFINE; g and amax for NVFP4 per gs).  fp_quantize /
+ * affine_quantize of "mlx 0.30.7.3 -> 0.30.7.6" (quantized.h, quantized.cpp
+ * fast::Quantize::eval_gpu).  gs is a bsfp_gs value and is ignored unless
+ * mode is NVFP4.  Codes and scales are bit-exact to the documented rules.
+ */
+bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                          bsfp_stream stream);
+
+/*
+ * bsfp_dequantize: q -> bf16 out [q->rows, q->cols].  fp_dequantize /
+ * affine_dequantize of "mlx 0.30.7.3 -> 0.30.7.6" (quantized.cpp).
+ *   NVFP4  bf16((E2M1 * E4M3) * g)  (g = 1 when q->global_scale is NULL)
+ *   MXFP4  bf16(E2M1 * 2^(S-127))
+ *   AFFINE bf16(fma(s, q, b))
+ */
+bsfp_status bsfp_dequantize(const bsfp_qtensor* q, uint16_t* out,
+                            bsfp_stream stream);
+
+/*
+ * bsfp_qmv: decode GEMV, y[m, n] = sum_k x[m, k] * dq(W)[n, k] for
+ * m < M <= 8, with W = w [N = w->rows, K = w->cols] and x bf16 [M, K].
+ * Weights are dequantized in registers and accumulated in fp32; y is bf16
+ * [M, N] (round to nearest even).  NVFP4 includes W's global scale when
+ * present.  ("epic: NVIDIA Volta (sm_70) inference acceleration program",
+ * Diagnosis item 3: qmv must accumulate in float; fp_qmv(w, scales, x, out,
+ * bits, group_size, M, N, K) in "mlx 0.30.7.3 -> 0.30.7.6", qqmm.cpp.)
+ */
+bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
+                     uint16_t* y, bsfp_stream stream);
+
+/*
+ * bsfp_qmm_workspace_bytes: device scratch bytes that bsfp_qmm needs for
+ * (mode, M, K, act): for BSFP_ACT_SAME, x's codes, scales and (NVFP4) amax
+ * and g; 0 for BSFP_ACT_BF16.  Returns 0 for unsupported arguments.
+ */
+size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act);
+
+/*
+ * bsfp_qmm: prefill GEMM on MFMA, y bf16 [M, N] with N = w->rows,
+ * K = w->cols, x bf16 [M, K] row-major, W in the "transposed" MLX layout
+ * [N, K] (QQMatmul::eval_gpu, w_transposed = true, lda = ldb = K:
+ * "mlx 0.30.7.3 -> 0.30.7.6", qqmm.cpp).
+ *   act == BSFP_ACT_BF16: y = x . dq(W)^T (bf16 MFMA, W dequantized in LDS).
+ *   act == BSFP_ACT_SAME: x is quantized into `workspace` with W's mode
+ *     (quantize_input in the same file), then y = alpha * dq0(q(x)) .
+ *     dq0(W)^T, dq0 = dequantization without the global scale, alpha =
+ *     g_x * g_w for NVFP4 with a global scale on W (g_x = amax_x/2688,
+ *     computed here), else 1.  The pages' alpha = amax_x*amax_w/(448*6)^2
+ *     (create_nvfp4_scalars) is the same quantity up to fp32 rounding.
+ *     MXFP4 runs on the gfx950 scaled f8f6f4 MFMA; NVFP4 and AFFINE on bf16
+ *     MFMA with both operands dequantized exactly.
+ * fp32 accumulation, bf16 (RNE) output.  `workspace` must hold
+ * bsfp_qmm_workspace_bytes(...) bytes (16-byte aligned) and is overwritten.
+ */
+bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
+                     int32_t act, void* workspace, size_t workspace_bytes,
+                     uint16_t* y, bsfp_stream stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* bsfp_last_error(void);
+
+/* Library version and the GPU architecture it was compiled for. */
+const char* bsfp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP_H */

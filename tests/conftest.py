@@ -31,3 +31,22 @@ def oracle_mod():
     from oracle import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr before it runs (uncaptured), so that a
+    run that dies inside a kernel still shows which case it was."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="session")
+def bsfp():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_scaled_bit_fp_amd as b
+    b.lib()
+    return b

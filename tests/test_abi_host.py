@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads, exports every entry point include/bsfp.h declares, and
+rejects bad arguments with a status and a message before touching the GPU."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsfp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsfp_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def blib():
+    import block_scaled_bit_fp_amd as b
+    return b
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for f in ("bsfp_quantize", "bsfp_dequantize", "bsfp_qmv", "bsfp_qmm", "bsfp_amax",
+              "bsfp_qmm_workspace_bytes", "bsfp_last_error", "bsfp_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(blib):
+    out = subprocess.run(["nm", "-D", "--defined-only", blib.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (bsfp_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    L = blib.lib()
+    for f in declared_functions():
+        assert hasattr(L, f)
+    assert "gfx950" in blib.version()
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "bsfp.h"\nint main(void){bsfp_qtensor q; (void)q; return 0;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    "-c", str(src), "-o", str(tmp_path / "t.o")], check=True)
+
+
+FAKE = 0x10000  # 16-byte aligned fake device address; never dereferenced
+
+
+def desc(blib, mode=2, bits=4, group=16, rows=4, cols=64, codes=FAKE, scales=FAKE,
+         biases=None, gs=None, amax=None):
+    return blib.QTensorDesc(mode, bits, group, rows, cols, codes, scales, biases, gs, amax)
+
+
+def status(blib, rc):
+    return blib.STATUS[rc], blib.lib().bsfp_last_error().decode()
+
+
+@pytest.mark.parametrize("mode,bits,group", [(3, 4, 16), (2, 8, 16), (2, 4, 32), (1, 4, 16),
+                                             (0, 4, 32), (0, 4, 128), (-1, 4, 64)])
+def test_unsupported_formats_are_reported_not_thrown(blib, mode, bits, group):
+    d = desc(blib, mode, bits, group)
+    rc = blib.lib().bsfp_quantize(C.c_void_p(FAKE), C.byref(d), 0, None)
+    st, msg = status(blib, rc)
+    assert st == "BSFP_ERR_UNSUPPORTED"
+    assert "supported" in msg and "(nvfp4, 4, 16)" in msg
+    rc = blib.lib().bsfp_qmv(C.c_void_p(FAKE), 1, C.byref(d), C.c_void_p(FAKE), None)
+    assert status(blib, rc)[0] == "BSFP_ERR_UNSUPPORTED"
+
+
+def test_bad_arguments(blib):
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    # cols not a multiple of the group
+    d = desc(blib, cols=40)
+    assert status(blib, L.bsfp_quantize(X, C.byref(d), 0, None))[0] == "BSFP_ERR_ARG"
+    # null codes
+    d = desc(blib, codes=None)
+    assert status(blib, L.bsfp_dequantize(C.byref(d), X, None))[0] == "BSFP_ERR_ARG"
+    # misaligned codes / x
+    d = desc(blib, codes=FAKE + 4)
+    assert status(blib, L.bsfp_dequantize(C.byref(d), X, None))[0] == "BSFP_ERR_ARG"
+    d = desc(blib)
+    assert status(blib, L.bsfp_quantize(C.c_void_p(FAKE + 2), C.byref(d), 0, None))[0] == "BSFP_ERR_ARG"
+    # NVFP4 global scale requested without buffers
+    assert status(blib, L.bsfp_quantize(X, C.byref(d), 1, None))[0] == "BSFP_ERR_ARG"
+    d2 = desc(blib, gs=FAKE)
+    assert status(blib, L.bsfp_quantize(X, C.byref(d2), 1, None))[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_quantize(X, C.byref(d2), 7, None))[0] == "BSFP_ERR_ARG"
+    # affine without biases
+    d = desc(blib, mode=0, group=64)
+    assert status(blib, L.bsfp_dequantize(C.byref(d), X, None))[0] == "BSFP_ERR_ARG"
+    # qmv M range
+    d = desc(blib)
+    for M in (0, 9, -1):
+        assert status(blib, L.bsfp_qmv(X, M, C.byref(d), X, None))[0] == "BSFP_ERR_ARG"
+    # null descriptor
+    assert status(blib, L.bsfp_qmv(X, 1, None, X, None))[0] == "BSFP_ERR_ARG"
+    # amax
+    assert status(blib, L.bsfp_amax(X, -1, X, None))[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_amax(X, 8, None, None))[0] == "BSFP_ERR_ARG"
+    # qmm: bad activation mode, K not a multiple of 32, missing workspace
+    assert status(blib, L.bsfp_qmm(X, 4, C.byref(d), 5, None, 0, X, None))[0] == "BSFP_ERR_ARG"
+    d48 = desc(blib, cols=48)
+    assert status(blib, L.bsfp_qmm(X, 4, C.byref(d48), 0, None, 0, X, None))[0] in (
+        "BSFP_ERR_ARG", "BSFP_ERR_UNSUPPORTED")
+    need = L.bsfp_qmm_workspace_bytes(2, 4, 64, 1)
+    if need:
+        rc = L.bsfp_qmm(X, 4, C.byref(d), 1, X, need - 1, X, None)
+        assert status(blib, rc)[0] == "BSFP_ERR_ARG"
+
+
+def test_workspace_query(blib):
+    L = blib.lib()
+    assert L.bsfp_qmm_workspace_bytes(9, 4, 64, 0) == 0
+    assert L.bsfp_qmm_workspace_bytes(2, -1, 64, 0) == 0
+    assert L.bsfp_qmm_workspace_bytes(2, 4, 64, 3) == 0
+    assert L.bsfp_qmm_workspace_bytes(2, 4, 64, 0) == 0  # weight-only needs none
+
+
+def test_no_cpu_fallback_in_product(blib):
+    """The product package never reaches the oracle (no import, no call)."""
+    pkg = os.path.dirname(blib.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, f

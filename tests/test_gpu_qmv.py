@@ -1,0 +1,138 @@
+"""GPU parity: decode GEMV (bsfp_qmv) against the oracle's fp64 product.
+
+Bar: normalized error |y - y_ref| / sum_k |x_k w_k| <= 3e-3 (the pages'
+~3e-3 relative bf16 tolerance against a dequantized f32 reference,
+"feat(quant): backend quantization capability table ...", 2026-09-29
+update).  Derivation for this path: bf16 output rounding contributes at most
+2^-9 (1.95e-3) and fp32 accumulation over K <= 25600 well under 1e-3.
+One-hot cases pin indexing exactly."""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as S
+from gpu_util import from_dev, oracle_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-3
+
+
+def run_qmv(o, b, x_bits, qo):
+    qd = oracle_to_dev(b, o, qo)
+    y = b.qmv(to_dev(x_bits), qd)
+    torch.cuda.synchronize()
+    return from_dev(y)
+
+
+def check(o, b, x_bits, qo, tol=TOL):
+    y = run_qmv(o, b, x_bits, qo)
+    yref, den = o.matmul_wonly(x_bits, qo)
+    e = o.norm_err(y, yref, den)
+    assert np.isfinite(e).all()
+    assert e.max() <= tol, (e.max(), np.unravel_index(e.argmax(), e.shape))
+    return e
+
+
+def test_affine_small_config(oracle_mod, bsfp):
+    x, w = S.affine_small()
+    e = check(oracle_mod, bsfp, x, oracle_mod.quantize(0, w))
+    assert e.max() <= 2 ** -8
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(37, 64 * 5), (300, 2880), (129, 5120), (17, 64 * 201)])
+def test_qmv_ragged(oracle_mod, bsfp, mode, M, N, K):
+    if mode == 1 and K % 32:
+        pytest.skip("K must be a multiple of 32")
+    x = S.generic((M, K), 1.0, seed=300 + M, stream=K)
+    w = S.generic((N, K), 0.02, seed=301 + mode, stream=N)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+def test_nvfp4_k_not_multiple_of_32(oracle_mod, bsfp):
+    for M in (1, 4):
+        for K in (16, 48, 16 * 33):
+            x = S.generic((M, K), 1.0, seed=K)
+            w = S.generic((70, K), 0.02, seed=K + 1)
+            check(oracle_mod, bsfp, x, oracle_mod.quantize(2, w))
+
+
+def test_nvfp4_without_global_scale(oracle_mod, bsfp):
+    x = S.generic((2, 1024), 1.0, seed=5)
+    w = S.generic((100, 1024), 0.02, seed=6)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(2, w, use_global=False))
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_affine_decode_full_size(oracle_mod, bsfp, which):
+    x, w = S.affine_decode(which)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(0, w))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_mxfp4_config_full_size(oracle_mod, bsfp, M):
+    w = S.mxfp4_weights()
+    x = S.mxfp4_activations(M)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(1, w))
+
+
+def test_nvfp4_prefill_weight_decode(oracle_mod, bsfp):
+    x = S.generic((1, 5120), 1.0, seed=8)
+    _, w = S.nvfp4_prefill(M=1, N=4096)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(2, w))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_onehot_activations_select_columns(oracle_mod, bsfp, mode):
+    """x = e_j: y[n] = bf16(w_hat[n, j]) (bit-exact for MXFP4 and for NVFP4
+    with a power-of-two global scale; at most one bf16 step otherwise)."""
+    o = oracle_mod
+    K, N = 64 * 9, 77
+    w = S.generic((N, K), 0.02, seed=400 + mode)
+    qo = o.quantize(mode, w, use_global=False) if mode == 2 else o.quantize(mode, w)
+    B = o.dequant_exact(qo)
+    for j in (0, 1, 5, 8, 31, 32, 100, K - 1):
+        x = np.zeros((1, K), np.uint16)
+        x[0, j] = 0x3F80
+        y = o.bf16_to_f32(run_qmv(o, bsfp, x, qo)[0]).astype(np.float64)
+        ref = o.bf16_to_f32(o.bf16_from_f64(B[:, j])).astype(np.float64)
+        if mode == 0:
+            assert np.all(np.abs(y - ref) <= np.abs(ref) * 2 ** -7 + 1e-30), j
+        else:
+            assert np.array_equal(y, ref), j
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_onehot_weights_select_activations(oracle_mod, bsfp, mode):
+    """Each weight row holds one 1.0 (unit scales): y[m, n] = x[m, j_n]."""
+    o = oracle_mod
+    K, N, M = 64 * 6, 50, 3
+    rng = np.random.default_rng(60 + mode)
+    j = rng.integers(0, K, N)
+    x = S.generic((M, K), 1.0, seed=61 + mode)
+    codes = np.zeros((N, K), np.int64)
+    if mode == 0:
+        codes[np.arange(N), j] = 1
+        scales = np.full((N, K // 64), 0x3F80, np.uint16)
+        biases = np.zeros((N, K // 64), np.uint16)
+    else:
+        codes[np.arange(N), j] = 2
+        scales = np.full((N, K // o.GROUP[mode]), 127 if mode == 1 else 0x38, np.uint8)
+        biases = None
+    wd = np.zeros((N, K // 8), np.uint32)
+    for k in range(8):
+        wd |= codes[:, k::8].astype(np.uint32) << (4 * k)
+    qo = o.QTensor(mode, N, K, wd, scales, biases, None)
+    y = run_qmv(o, bsfp, x, qo)
+    assert np.array_equal(o.bf16_to_f32(y), o.bf16_to_f32(x[:, j]))
+
+
+def test_qmv_deterministic(bsfp):
+    x = to_dev(S.generic((1, 5120), 1.0, seed=1))
+    w = to_dev(S.generic((4096, 5120), 0.02, seed=2))
+    for mode in (0, 1, 2):
+        q = bsfp.quantize(w, mode)
+        a = bsfp.qmv(x, q)
+        b2 = bsfp.qmv(x, q)
+        assert torch.equal(a, b2)

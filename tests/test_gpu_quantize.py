@@ -1,0 +1,148 @@
+"""GPU parity: amax, quantize and dequantize through the C ABI against the
+oracle.  The bar is bit-exact codes, scales, global scale and dequantized
+values (the pages' own test design: GPU quantize bit-identical to the CPU
+quantizer at 4096x4096, "feat(quant): backend quantization capability table
+...", the 2026-09-29 update)."""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as S
+from gpu_util import from_dev, qt_to_oracle, to_dev, u8, words
+
+pytestmark = pytest.mark.gpu
+
+MODES = [0, 1, 2]
+
+
+def check_quant_exact(o, b, x_bits, mode, gs="compute", g=None):
+    xd = to_dev(x_bits)
+    gd = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda")
+    q = b.quantize(xd, mode, global_scale=gs, g=gd)
+    if mode == o.NVFP4:
+        qo = o.quantize(mode, x_bits, use_global=(gs != "none"), g=g)
+    else:
+        qo = o.quantize(mode, x_bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(q.codes), qo.codes), "codes differ"
+    if mode == o.AFFINE:
+        assert np.array_equal(from_dev(q.scales), qo.scales)
+        assert np.array_equal(from_dev(q.biases), qo.biases)
+    else:
+        assert np.array_equal(u8(q.scales), qo.scales), "scales differ"
+    if mode == o.NVFP4 and gs != "none":
+        assert q.global_scale.item() == qo.g
+        if gs == "compute":
+            assert q.amax.item() == qo.amax
+    # dequantize, bit-exact
+    dq = from_dev(b.dequantize(q))
+    assert np.array_equal(dq, o.dequantize(qo)), "dequantized values differ"
+    return q, qo
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(1, 64), (37, 64 * 13), (3, 2880), (129, 5120)])
+def test_quantize_ragged_shapes(oracle_mod, bsfp, mode, shape):
+    x = S.generic(shape, 1.5, seed=200 + mode, stream=shape[0])
+    check_quant_exact(oracle_mod, bsfp, x, mode)
+
+
+def test_nvfp4_activation_config_bit_exact(oracle_mod, bsfp):
+    """X[4096,5120] ~ N(0,1) with 1 % outliers at +-20: codes, scales, g and
+    amax bit-exact; the dequantization round trip bit-exact too."""
+    x = S.nvfp4_activations()
+    q, qo = check_quant_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4)
+    assert qo.amax == np.float32(20.0)
+
+
+def test_nvfp4_given_and_no_global_scale(oracle_mod, bsfp):
+    x = S.generic((64, 1024), 0.02, seed=210)
+    check_quant_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4, gs="given", g=3.7e-5)
+    check_quant_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4, gs="given", g=1e-9)  # saturating
+    check_quant_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4, gs="none")
+
+
+def test_mxfp4_weight_config_bit_exact(oracle_mod, bsfp):
+    check_quant_exact(oracle_mod, bsfp, S.mxfp4_weights(), oracle_mod.MXFP4)
+
+
+def test_affine_weight_configs_bit_exact(oracle_mod, bsfp):
+    _, w = S.affine_small()
+    check_quant_exact(oracle_mod, bsfp, w, oracle_mod.AFFINE)
+    _, w = S.affine_decode("up")
+    check_quant_exact(oracle_mod, bsfp, w, oracle_mod.AFFINE)
+
+
+def _all_bf16_blocks():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(f) & (np.abs(f) < 1e36)]
+    n = (bits.size // 64) * 64
+    return bits[:n].reshape(-1, 64)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_every_bf16_value(oracle_mod, bsfp, mode):
+    """All finite bf16 values (|x| < 1e36, so affine ranges stay finite), in
+    order and shuffled, through each quantizer."""
+    x = _all_bf16_blocks()
+    check_quant_exact(oracle_mod, bsfp, x, mode, gs="none" if mode == 2 else "compute")
+    rng = np.random.default_rng(5)
+    xs = rng.permutation(x.reshape(-1)).reshape(x.shape)
+    check_quant_exact(oracle_mod, bsfp, xs, mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_threshold_neighbourhoods(oracle_mod, bsfp, mode):
+    """Blocks whose scaled values sit on and next to every E2M1 decision
+    boundary (NVFP4 with g = 1 and MXFP4: the block max fixes the scale)."""
+    o = oracle_mod
+    rng = np.random.default_rng(77 + mode)
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    rows = []
+    G = o.GROUP[mode]
+    for _ in range(64):
+        scale = float(2.0 ** rng.integers(-6, 6))
+        v = rng.choice(bounds, G) * scale
+        v *= rng.choice([1 - 2 ** -7, 1.0, 1 + 2 ** -7], G)
+        v *= rng.choice([-1.0, 1.0], G)
+        v[0] = 6.0 * scale  # block max: NVFP4 scale 1*scale... exact E4M3
+        rows.append(v)
+    x = S.to_bf16_bits(np.array(rows, np.float32).reshape(-1, 64))
+    check_quant_exact(o, bsfp, x, mode, gs="none" if mode == 2 else "compute")
+
+
+def test_zero_and_tiny_tensors(oracle_mod, bsfp):
+    o = oracle_mod
+    for mode in MODES:
+        z = np.zeros((3, o.GROUP[mode] * 2), np.uint16)
+        check_quant_exact(o, bsfp, z, mode)
+    z = np.zeros((2, 64), np.uint16)
+    z[0, 5] = 0x8000  # -0
+    check_quant_exact(o, bsfp, z, o.NVFP4)
+    # a tensor so small that it is one group
+    check_quant_exact(o, bsfp, S.generic((1, 16), 1.0, seed=3), o.NVFP4)
+    check_quant_exact(o, bsfp, S.generic((1, 32), 1.0, seed=3), o.MXFP4)
+
+
+def test_empty_tensor(bsfp):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    for mode in MODES:
+        q = bsfp.quantize(x, mode)
+        assert q.codes.numel() == 0
+        assert bsfp.dequantize(q).numel() == 0
+
+
+def test_amax_matches_oracle(oracle_mod, bsfp):
+    for n in (1, 7, 8, 9, 1000, 4096 * 5120 + 5):
+        x = S.generic((n,), 2.0, seed=n % 1000)
+        got = bsfp.amax(to_dev(x)).item()
+        assert got == oracle_mod.amax(x), n
+    assert bsfp.amax(torch.zeros(0, dtype=torch.bfloat16, device="cuda")).item() == 0.0
+
+
+def test_quantize_is_deterministic(bsfp):
+    x = to_dev(S.nvfp4_activations(512, 5120, seed=9))
+    a = bsfp.quantize(x, 2)
+    b2 = bsfp.quantize(x, 2)
+    assert torch.equal(a.codes, b2.codes) and torch.equal(a.scales, b2.scales)
