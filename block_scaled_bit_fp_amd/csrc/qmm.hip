@@ -145,37 +145,44 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
   tn = b / tiles_m;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
+// including the direct-to-LDS ones the compiler does not track.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DEC, int WMT, int WNT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dq_kernel(
     const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
     const float* __restrict__ g1, const float* __restrict__ g2, int M, int N, int K,
     uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
-  constexpr int BM = 64 * WMT;
-  constexpr int ACH = BM / 32;  // 16-byte A chunks per thread per K step
-  extern __shared__ uint4 lds[];  // [2][BM][8] chunks, XOR-swizzled
+  constexpr int BM = 64 * WMT, BN = 64 * WNT;
+  constexpr int WROWS = BM / 4;  // A rows each wave brings into LDS per K step
+  extern __shared__ uint4 lds[];  // [2][BM][8] 16-byte chunks, XOR-swizzled
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
-  const int m_base = tm * BM, n_base = tn * (64 * WNT);
+  const int m_base = tm * BM, n_base = tn * BN;
 
-  uint4 areg[ACH];
-  auto load_a = [&](int k0) {
+  // A: direct global -> LDS, 16 bytes per lane per instruction; an
+  // instruction fills 8 consecutive tile rows (lane i -> row i / 8, physical
+  // chunk i % 8), so the swizzle is applied to the source addresses.
+  const uint16_t* a_src[WROWS / 8];
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-      const int q = tid + kThreads * c, r = q >> 3, ch = q & 7;
-      const int gm = min(m_base + r, M - 1);
-      areg[c] = *reinterpret_cast<const uint4*>(A + (int64_t)gm * K + k0 + ch * 8);
-    }
-  };
-  auto store_a = [&](int buf) {
+  for (int s = 0; s < WROWS / 8; ++s) {
+    const int r = wave * WROWS + s * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ (r & 7);
+    a_src[s] = A + (int64_t)min(m_base + r, M - 1) * K + lc * 8;
+  }
+  auto load_a = [&](int k0, int buf) {
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-      const int q = tid + kThreads * c, r = q >> 3, ch = q & 7;
-      lds[(buf * BM + r) * 8 + (ch ^ (r & 7))] = areg[c];
+    for (int s = 0; s < WROWS / 8; ++s) {
+      uint4* dst = lds + (buf * BM + wave * WROWS + s * 8) * 8;
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[s] + k0), (lds_void_t*)dst, 16, 0, 0);
     }
   };
 
@@ -196,50 +203,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_a(0);
+  load_a(0, 0);
   load_b(0);
-  store_a(0);
-  __syncthreads();
-
   for (int k0 = 0; k0 < K; k0 += 64) {
     const int buf = (k0 >> 6) & 1;
+    wait_vmem();      // this wave's loads for step k0 have landed
+    __syncthreads();  // ... and every wave's; nobody still reads buf ^ 1
+    // All A fragments of this step go to registers before the next step's
+    // direct-to-LDS loads are issued: the compiler cannot tell the two LDS
+    // buffers apart and would otherwise wait for those loads before reading.
+    uint4 a[4][WMT];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int r = wm * 32 * WMT + 32 * i + l32;
+        a[kk][i] = lds[(buf * BM + r) * 8 + ((4 * h + kk) ^ (r & 7))];
+      }
     BFrag bcur[WNT];
 #pragma unroll
     for (int j = 0; j < WNT; ++j) bcur[j] = bnext[j];
-    const bool more = k0 + 64 < K;
-    if (more) {
-      load_a(k0 + 64);
+    if (k0 + 64 < K) {
+      load_a(k0 + 64, buf ^ 1);
       load_b(k0 + 64);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      uint4 a[WMT];
-#pragma unroll
-      for (int i = 0; i < WMT; ++i) {
-        const int r = wm * 32 * WMT + 32 * i + l32;
-        a[i] = lds[(buf * BM + r) * 8 + ((4 * h + kk) ^ (r & 7))];
-      }
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const Op8 b = expand<DEC>(bcur[j], kk);
 #pragma unroll
-        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], b, acc[i][j]);
+        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[kk][i], b, acc[i][j]);
       }
     }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
   }
 
   const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
+  const bool full = (m_base + BM <= M) && (n_base + BN <= N);
 #pragma unroll
   for (int i = 0; i < WMT; ++i)
 #pragma unroll
     for (int j = 0; j < WNT; ++j) {
       const int n = n_base + wn * 32 * WNT + 32 * j + l32;
+      const int m0 = m_base + wm * 32 * WMT + 32 * i + 4 * h;
+      uint16_t* yp = Y + (int64_t)m0 * N + n;
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m_base + wm * 32 * WMT + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+        for (int r = 0; r < 16; ++r)
+          yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 8 * (r >> 2) + (r & 3);
+          if (m < M && n < N)
+            yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+        }
       }
     }
 }

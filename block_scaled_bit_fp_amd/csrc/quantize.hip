@@ -50,10 +50,23 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
   const int64_t nv = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   float m = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nv; i += stride) {
-    uint4 v = xv[i];
+  // four independent 16-byte loads in flight per lane
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nv; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float f[8];
+      unpack8(v[u], f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+    }
+  }
+  for (; i < nv; i += stride) {
     float f[8];
-    unpack8(v, f);
+    unpack8(xv[i], f);
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
   }
@@ -275,8 +288,8 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_
   hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax_out);
   if (n > 0) {
     const int64_t nv = n >> 3;
-    int grid = stream_grid(nv);
-    if (grid > device_cu_count() * 8) grid = device_cu_count() * 8;
+    int grid = stream_grid(nv / 4 + 1);
+    if (grid > device_cu_count() * 4) grid = device_cu_count() * 4;
     hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kThreads), 0, s, x, n, amax_out);
   }
   return hipGetLastError();
