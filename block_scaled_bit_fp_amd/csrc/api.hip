@@ -205,8 +205,12 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_
   if (act == BSFP_ACT_SAME && w->mode == BSFP_AFFINE)
     return fail(BSFP_ERR_UNSUPPORTED,
                 "bsfp_qmm: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only");
-  if (M > (1 << 30) || w->rows > (1 << 30) || w->cols > (1 << 30))
-    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: dimensions beyond 2^30");
+  if (M > (1 << 30) || w->rows > (1 << 30))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: M or N beyond 2^30");
+  // the GEMM addresses a 256-row activation tile with 32-bit byte offsets
+  if (w->cols > (1 << 22))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld beyond 2^22",
+                (long long)w->cols);
   const size_t need = qmm_workspace_bytes(w->mode, M, w->cols, act);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(BSFP_ERR_ARG, "bsfp_qmm: workspace needs %zu bytes (16-byte aligned), got %zu",

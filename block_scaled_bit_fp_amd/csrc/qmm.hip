@@ -84,16 +84,17 @@ __device__ __forceinline__ Op8 expand(const BFrag& f, int kk) {
   const uint32_t w = kk == 0 ? f.codes.x : kk == 1 ? f.codes.y : kk == 2 ? f.codes.z : f.codes.w;
   Op8 o;
   if constexpr (DEC == DEC_NVFP4_F16) {
-    const uint32_t sb = (kk < 2) ? (f.s0 & 0xFFu) : (f.s0 >> 8);
-    const _Float16 sh = (_Float16)e4m3_decode(sb);
+    // both E4M3 block scales -> fp16 with the hardware converter (exact)
+    const f16x2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s0, 1.0f, false);
+    const _Float16 sh = (kk < 2) ? sp.x : sp.y;
     const f16x2_t s2 = {sh, sh};
     o.v[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
     o.v[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
     o.v[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
     o.v[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
   } else if constexpr (DEC == DEC_NVFP4) {
-    const uint32_t sb = (kk < 2) ? (f.s0 & 0xFFu) : (f.s0 >> 8);
-    const float sc = e4m3_decode(sb);
+    const f32x2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.s0, 1.0f, false);
+    const float sc = (kk < 2) ? sp.x : sp.y;
     f32x2_t p0 = e2m1x2_to_f32x2<0>(w), p1 = e2m1x2_to_f32x2<1>(w);
     f32x2_t p2 = e2m1x2_to_f32x2<2>(w), p3 = e2m1x2_to_f32x2<3>(w);
     o.v[0] = pack_bf16x2(p0.x * sc, p0.y * sc);
@@ -146,53 +147,111 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): 32-bit offsets, loads past
+// the end return 0 (rows beyond M or N read as zeros).
+constexpr int kRawBufferFlags = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(uint32_t)bytes, kRawBufferFlags);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: the LDS base is
+// wave-uniform and lane i lands at base + 16 i.  (Kept out of line of the
+// kernel templates: the host pass of hipcc drops a kernel's launch stub when
+// its template body names this builtin directly.)
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
 
 // s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
 // including the direct-to-LDS ones the compiler does not track.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DEC, int WMT, int WNT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dq_kernel(
+// Physical 16-byte chunk of logical chunk c in tile row r.  The XOR with r & 7
+// spreads 8 consecutive rows over the 8 chunks of a 128-byte row; the extra
+// bit for rows 8..15 moves them to the other half of the 256-byte bank space,
+// so the 16 rows one ds_read_b128 pass touches hit 16 different bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Per-lane weight data of one 32-column subtile, loaded through buffer
+// descriptors based at the tile's first weight row.
+template <int DEC>
+__device__ __forceinline__ void load_bfrag_buf(BFrag& f, const rsrc_t& rc, const rsrc_t& rs,
+                                               const rsrc_t& rb, int nl, int K, int k0, int h) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, nl * (K / 2) + 16 * h, k0 / 2, 0);
+  f.codes = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+  if constexpr (DEC == DEC_AFFINE) {
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, nl * (K / 64) * 2, k0 / 32, 0);
+    f.s1 = __builtin_amdgcn_raw_buffer_load_b16(rb, nl * (K / 64) * 2, k0 / 32, 0);
+  } else if constexpr (DEC == DEC_MXFP4) {
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, nl * (K / 32) + h, k0 / 32, 0);
+  } else {  // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, nl * (K / 16) + 2 * h, k0 / 16, 0);
+  }
+}
+
+// WGM x WGN waves per workgroup, each owning WMT x WNT MFMA tiles of 32 x 32.
+template <int DEC, int WGM, int WGN, int WMT, int WNT>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
     const float* __restrict__ g1, const float* __restrict__ g2, int M, int N, int K,
     uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
-  constexpr int BM = 64 * WMT, BN = 64 * WNT;
-  constexpr int WROWS = BM / 4;  // A rows each wave brings into LDS per K step
-  extern __shared__ uint4 lds[];  // [2][BM][8] 16-byte chunks, XOR-swizzled
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
+  constexpr int WROWS = BM / NW;  // A rows each wave brings into LDS per K step
+  static_assert(WROWS % 8 == 0, "each wave loads whole 8-row LDS blocks");
+  // Two separate LDS arrays (not one array with a computed offset) let the
+  // compiler see that the prefetch into one never aliases reads of the other,
+  // so it does not hold the reads behind the prefetch.
+  __shared__ uint4 lds0[BM * 8];  // [BM][8] 16-byte chunks, swizzled
+  __shared__ uint4 lds1[BM * 8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
   const int m_base = tm * BM, n_base = tn * BN;
+  const int rows_m = min(BM, M - m_base), rows_n = min(BN, N - n_base);
 
-  // A: direct global -> LDS, 16 bytes per lane per instruction; an
-  // instruction fills 8 consecutive tile rows (lane i -> row i / 8, physical
-  // chunk i % 8), so the swizzle is applied to the source addresses.
-  const uint16_t* a_src[WROWS / 8];
+  // A: direct buffer -> LDS, 16 bytes per lane per instruction; an instruction
+  // fills 8 consecutive tile rows (lane i -> row i / 8, physical chunk i % 8),
+  // so the swizzle is applied to the source offsets.
+  const rsrc_t ra = make_rsrc(A + (int64_t)m_base * K, (int64_t)rows_m * K * 2);
+  int a_off[WROWS / 8];
 #pragma unroll
   for (int s = 0; s < WROWS / 8; ++s) {
     const int r = wave * WROWS + s * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ (r & 7);
-    a_src[s] = A + (int64_t)min(m_base + r, M - 1) * K + lc * 8;
+    a_off[s] = r * K * 2 + swz(r, lane & 7) * 16;
   }
-  auto load_a = [&](int k0, int buf) {
+  auto load_a = [&](int k0, uint4* buf) {
 #pragma unroll
     for (int s = 0; s < WROWS / 8; ++s) {
-      uint4* dst = lds + (buf * BM + wave * WROWS + s * 8) * 8;
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[s] + k0), (lds_void_t*)dst, 16, 0, 0);
+      uint4* dst = buf + (wave * WROWS + s * 8) * 8;
+      buffer_load_lds16(ra, dst, a_off[s], k0 * 2);
     }
   };
 
-  int64_t nrow[WNT];
+  // B: the lane's weight rows within the tile
+  const rsrc_t rc = make_rsrc(codes + (int64_t)n_base * (K / 8), (int64_t)rows_n * (K / 2));
+  constexpr int gsz = (DEC == DEC_AFFINE) ? 64 : (DEC == DEC_MXFP4) ? 32 : 16;
+  constexpr int sbytes = (DEC == DEC_AFFINE) ? 2 : 1;
+  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) +
+                                  (int64_t)n_base * (K / gsz) * sbytes,
+                              (int64_t)rows_n * (K / gsz) * sbytes);
+  const rsrc_t rb = make_rsrc(biases ? biases + (int64_t)n_base * (K / 64) : nullptr,
+                              biases ? (int64_t)rows_n * (K / 64) * 2 : 0);
+  int nl[WNT];
 #pragma unroll
-  for (int j = 0; j < WNT; ++j) nrow[j] = min(n_base + wn * 32 * WNT + 32 * j + l32, N - 1);
-  BFrag bnext[WNT];
-  auto load_b = [&](int k0) {
+  for (int j = 0; j < WNT; ++j) nl[j] = wn * 32 * WNT + 32 * j + l32;
+  auto load_b = [&](int k0, BFrag (&dst)[WNT]) {
 #pragma unroll
-    for (int j = 0; j < WNT; ++j) load_bfrag<DEC>(bnext[j], codes, scales, biases, nrow[j], K, k0, h);
+    for (int j = 0; j < WNT; ++j) load_bfrag_buf<DEC>(dst[j], rc, rs, rb, nl[j], K, k0, h);
   };
 
   f32x16_t acc[WMT][WNT];
@@ -203,43 +262,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_a(0, 0);
-  load_b(0);
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    const int buf = (k0 >> 6) & 1;
-    wait_vmem();      // this wave's loads for step k0 have landed
-    __syncthreads();  // ... and every wave's; nobody still reads buf ^ 1
-    // All A fragments of this step go to registers before the next step's
-    // direct-to-LDS loads are issued: the compiler cannot tell the two LDS
-    // buffers apart and would otherwise wait for those loads before reading.
-    uint4 a[4][WMT];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < WMT; ++i) {
-        const int r = wm * 32 * WMT + 32 * i + l32;
-        a[kk][i] = lds[(buf * BM + r) * 8 + ((4 * h + kk) ^ (r & 7))];
-      }
-    BFrag bcur[WNT];
-#pragma unroll
-    for (int j = 0; j < WNT; ++j) bcur[j] = bnext[j];
+  // One K step: wait until every wave's loads for this step have landed,
+  // issue the next step's loads into the other buffer, then run the MFMAs.
+  auto step = [&](int k0, uint4* cur_lds, uint4* nxt_lds, BFrag (&cur)[WNT],
+                  BFrag (&nxt)[WNT]) {
+    wait_vmem();
+    __syncthreads();
     if (k0 + 64 < K) {
-      load_a(k0 + 64, buf ^ 1);
-      load_b(k0 + 64);
+      load_a(k0 + 64, nxt_lds);
+      load_b(k0 + 64, nxt);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      uint4 a[WMT];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int r = wm * 32 * WMT + 32 * i + l32;
+        a[i] = cur_lds[r * 8 + swz(r, 4 * h + kk)];
+      }
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        const Op8 b = expand<DEC>(bcur[j], kk);
+        const Op8 b = expand<DEC>(cur[j], kk);
 #pragma unroll
-        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[kk][i], b, acc[i][j]);
+        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], b, acc[i][j]);
       }
     }
+  };
+
+  BFrag b0[WNT], b1[WNT];
+  load_a(0, lds0);
+  load_b(0, b0);
+  for (int k0 = 0; k0 < K; k0 += 128) {
+    step(k0, lds0, lds1, b0, b1);
+    if (k0 + 64 < K) step(k0 + 64, lds1, lds0, b1, b0);
   }
 
   const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
-  const bool full = (m_base + BM <= M) && (n_base + BN <= N);
+  const bool full = (rows_m == BM) && (rows_n == BN);
 #pragma unroll
   for (int i = 0; i < WMT; ++i)
 #pragma unroll
@@ -341,26 +400,27 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     }
 }
 
-template <int DEC, int WMT>
+template <int DEC, int WGM, int WGN, int WMT, int WNT>
 hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
                   const float* g2, uint16_t* y, hipStream_t s) {
-  constexpr int WNT = 4;
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
   const int N = (int)w.rows, K = (int)w.cols;
-  const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
-  const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
-  const size_t lds = (size_t)2 * 64 * WMT * 8 * sizeof(uint4);
-  hipLaunchKernelGGL((gemm_dq_kernel<DEC, WMT, WNT>), dim3(tiles_m * tiles_n), dim3(kThreads),
-                     lds, s, A, w.codes, w.scales, w.biases, g1, g2, M, N, K, y, tiles_m,
-                     tiles_n);
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>), dim3(tiles_m * tiles_n),
+                     dim3(64 * WGM * WGN), 0, s, A, w.codes, w.scales, w.biases, g1, g2, M, N,
+                     K, y, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
+// Tile shapes: 256 x 256 with 8 waves (each 128 x 64) for prefill row
+// counts; narrower M tiles for small M.
 template <int DEC>
 hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
                     const float* g2, uint16_t* y, hipStream_t s) {
-  if (M <= 64) return run_dq<DEC, 1>(A, M, w, g1, g2, y, s);
-  if (M <= 128) return run_dq<DEC, 2>(A, M, w, g1, g2, y, s);
-  return run_dq<DEC, 4>(A, M, w, g1, g2, y, s);
+  if (M <= 64) return run_dq<DEC, 1, 4, 2, 2>(A, M, w, g1, g2, y, s);
+  if (M <= 128) return run_dq<DEC, 2, 4, 2, 2>(A, M, w, g1, g2, y, s);
+  return run_dq<DEC, 2, 4, 4, 2>(A, M, w, g1, g2, y, s);
 }
 
 hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,

@@ -1,0 +1,483 @@
+// qmm.hip -- prefill GEMM y[M, N] = x[M, K] . W[N, K]^T on MFMA for gfx950.
+//
+// Two kernels share one tiling scheme (4 waves in a 2 x 2 arrangement, each
+// wave owning WMT x WNT tiles of 32 x 32 outputs, K advanced 64 at a time):
+//
+// gemm_dq_kernel -- 16-bit MFMA (v_mfma_f32_32x32x16_{bf16,f16}) with the
+//   weights dequantized in registers.  The 16-bit A operand (bf16 x, or the
+//   fp16 dequantized NVFP4 activations of the qq path) is staged through LDS
+//   (double-buffered, XOR-swizzled 16-byte chunks so the 32 rows a wave reads
+//   at one k offset fall in different banks).  The packed weight codes never
+//   touch LDS: each lane loads the 16-byte code chunk (32 k-values) of its
+//   own weight row one K-step ahead and expands it right before the MFMA.
+//   The contraction order inside a 64-wide K step is permuted consistently
+//   for both operands: at MFMA step kk, lane half h covers k = 32h + 8kk ..
+//   32h + 8kk + 7, so that each lane reads whole code words.
+//     NVFP4 qq (fp16): E2M1 * E4M3 is exact in fp16, so the weight expands
+//       with one v_cvt_scalef32_pk_f16_fp4 and one v_pk_mul_f16 per pair.
+//     NVFP4 weight-only (bf16): E2M1 -> fp32 pair, times the block scale,
+//       packed to bf16 (exact).
+//     MXFP4 weight-only (bf16): v_cvt_scalef32_pk_bf16_fp4 with the E8M0
+//       block scale as the converter's exponent scale (exact).
+//     affine weight-only (bf16): s * q + b rounded once to bf16 (the
+//       "dequantize to bf16, then a bf16 GEMM" numerics of "mlx: opt-in dense
+//       GEMM for nvfp4 prefill"); q comes from the exact fp8-byte decode.
+//   The per-tensor scale (g_w, or alpha = g_x * g_w for qq) is applied in the
+//   epilogue ("mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu: alpha =
+//   amax_x * amax_w / (448*6)^2, read on the device).
+//
+// gemm_mx_kernel -- MXFP4 x MXFP4 on the CDNA4 block-scaled MFMA
+//   v_mfma_scale_f32_32x32x64_f8f6f4: both operands stay 4-bit, and each
+//   lane hands the MFMA the E8M0 scale of the 32 k-values it holds, which is
+//   exactly one MXFP4 group.  No dequantization at all.
+//
+// fp32 accumulation, bf16 round-to-nearest-even output, rows and columns
+// beyond M / N clamped on load and masked on store.
+#include "bsfp_device.hpp"
+#include "bsfp_internal.hpp"
+
+namespace bsfp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+enum { DEC_AFFINE = 0, DEC_MXFP4 = 1, DEC_NVFP4 = 2, DEC_NVFP4_F16 = 3 };
+
+// Expanded B operand of one MFMA (8 consecutive k of one weight row).
+struct Op8 {
+  uint32_t v[4];
+};
+
+// Per-lane per-K-step weight data of one 32-column subtile.
+struct BFrag {
+  uint4 codes;   // 32 codes: k = k0 + 32h + 0..31
+  uint32_t s0;   // scale bits (mode specific)
+  uint32_t s1;   // affine bias bits
+};
+
+template <int DEC>
+__device__ __forceinline__ void load_bfrag(BFrag& f, const uint32_t* __restrict__ codes,
+                                           const void* __restrict__ scales,
+                                           const uint16_t* __restrict__ biases, int64_t n,
+                                           int K, int k0, int h) {
+  f.codes = *reinterpret_cast<const uint4*>(codes + n * (K / 8) + (k0 / 8) + 4 * h);
+  if constexpr (DEC == DEC_AFFINE) {
+    const int64_t gi = n * (K / 64) + k0 / 64;
+    f.s0 = reinterpret_cast<const uint16_t*>(scales)[gi];
+    f.s1 = biases[gi];
+  } else if constexpr (DEC == DEC_MXFP4) {
+    f.s0 = reinterpret_cast<const uint8_t*>(scales)[n * (K / 32) + k0 / 32 + h];
+  } else {  // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
+    f.s0 = reinterpret_cast<const uint16_t*>(scales)[n * (K / 32) + k0 / 32 + h];
+  }
+}
+
+// Expand word kk of the fragment (k = 32h + 8kk + 0..7).
+template <int DEC>
+__device__ __forceinline__ Op8 expand(const BFrag& f, int kk) {
+  const uint32_t w = kk == 0 ? f.codes.x : kk == 1 ? f.codes.y : kk == 2 ? f.codes.z : f.codes.w;
+  Op8 o;
+  if constexpr (DEC == DEC_NVFP4_F16) {
+    // both E4M3 block scales -> fp16 with the hardware converter (exact)
+    const f16x2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s0, 1.0f, false);
+    const _Float16 sh = (kk < 2) ? sp.x : sp.y;
+    const f16x2_t s2 = {sh, sh};
+    o.v[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
+    o.v[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
+    o.v[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
+    o.v[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
+  } else if constexpr (DEC == DEC_NVFP4) {
+    const f32x2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.s0, 1.0f, false);
+    const float sc = (kk < 2) ? sp.x : sp.y;
+    f32x2_t p0 = e2m1x2_to_f32x2<0>(w), p1 = e2m1x2_to_f32x2<1>(w);
+    f32x2_t p2 = e2m1x2_to_f32x2<2>(w), p3 = e2m1x2_to_f32x2<3>(w);
+    o.v[0] = pack_bf16x2(p0.x * sc, p0.y * sc);
+    o.v[1] = pack_bf16x2(p1.x * sc, p1.y * sc);
+    o.v[2] = pack_bf16x2(p2.x * sc, p2.y * sc);
+    o.v[3] = pack_bf16x2(p3.x * sc, p3.y * sc);
+  } else if constexpr (DEC == DEC_MXFP4) {
+    const float sc = __uint_as_float(f.s0 << 23);  // the converter reads its exponent only
+    o.v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    o.v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    o.v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    o.v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  } else {  // affine: s * q + b, one rounding to bf16
+    const float s = __uint_as_float(f.s0 << 16), b = __uint_as_float(f.s1 << 16);
+    const uint32_t t = w & 0x0F0F0F0Fu, u = (w >> 4) & 0x0F0F0F0Fu;
+    // t holds q0, q2, q4, q6 in its bytes; u holds q1, q3, q5, q7
+    const f32x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, false);  // q0, q2
+    const f32x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, true);   // q4, q6
+    const f32x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, false);  // q1, q3
+    const f32x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, true);   // q5, q7
+    o.v[0] = pack_bf16x2(__builtin_fmaf(s, a0.x, b), __builtin_fmaf(s, b0.x, b));
+    o.v[1] = pack_bf16x2(__builtin_fmaf(s, a0.y, b), __builtin_fmaf(s, b0.y, b));
+    o.v[2] = pack_bf16x2(__builtin_fmaf(s, a1.x, b), __builtin_fmaf(s, b1.x, b));
+    o.v[3] = pack_bf16x2(__builtin_fmaf(s, a1.y, b), __builtin_fmaf(s, b1.y, b));
+  }
+  return o;
+}
+
+template <int DEC>
+__device__ __forceinline__ f32x16_t mfma16(const uint4& a, const Op8& b, const f32x16_t& c) {
+  const uint4 bv = {b.v[0], b.v[1], b.v[2], b.v[3]};
+  if constexpr (DEC == DEC_NVFP4_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+  }
+}
+
+// XCD-aware tile order: workgroup b runs on XCD b % 8, so consecutive logical
+// tiles (which share a weight column block across the M tiles) are given to
+// workgroups of one XCD and hit the same L2.
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {
+  int b = blockIdx.x;
+  const int T = tiles_m * tiles_n;
+  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+  tm = b % tiles_m;
+  tn = b / tiles_m;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer straight into LDS (M0 = wave base, lane i
+// lands at base + 16 i).
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): 32-bit offsets, loads past
+// the end return 0 (rows beyond M or N read as zeros).
+constexpr int kRawBufferFlags = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kRawBufferFlags);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
+// including the direct-to-LDS ones the compiler does not track.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Physical 16-byte chunk of logical chunk c in tile row r.  The XOR with r & 7
+// spreads 8 consecutive rows over the 8 chunks of a 128-byte row; the extra
+// bit for rows 8..15 moves them to the other half of the 256-byte bank space,
+// so the 16 rows one ds_read_b128 pass touches hit 16 different bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Per-lane weight data of one 32-column subtile, loaded through buffer
+// descriptors based at the tile's first weight row.
+template <int DEC>
+__device__ __forceinline__ void load_bfrag_buf(BFrag& f, const rsrc_t& rc, const rsrc_t& rs,
+                                               const rsrc_t& rb, int nl, int K, int k0, int h) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, nl * (K / 2) + 16 * h, k0 / 2, 0);
+  f.codes = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+  if constexpr (DEC == DEC_AFFINE) {
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, nl * (K / 64) * 2, k0 / 32, 0);
+    f.s1 = __builtin_amdgcn_raw_buffer_load_b16(rb, nl * (K / 64) * 2, k0 / 32, 0);
+  } else if constexpr (DEC == DEC_MXFP4) {
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, nl * (K / 32) + h, k0 / 32, 0);
+  } else {  // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
+    f.s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, nl * (K / 16) + 2 * h, k0 / 16, 0);
+  }
+}
+
+// WGM x WGN waves per workgroup, each owning WMT x WNT MFMA tiles of 32 x 32.
+template <int DEC, int WGM, int WGN, int WMT, int WNT>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
+    const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
+    const void* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const float* __restrict__ g1, const float* __restrict__ g2, int M, int N, int K,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
+  constexpr int WROWS = BM / NW;  // A rows each wave brings into LDS per K step
+  static_assert(WROWS % 8 == 0, "each wave loads whole 8-row LDS blocks");
+  // Two separate LDS arrays (not one array with a computed offset) let the
+  // compiler see that the prefetch into one never aliases reads of the other,
+  // so it does not hold the reads behind the prefetch.
+  __shared__ uint4 lds0[BM * 8];  // [BM][8] 16-byte chunks, swizzled
+  __shared__ uint4 lds1[BM * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int h = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m_base = tm * BM, n_base = tn * BN;
+  const int rows_m = min(BM, M - m_base), rows_n = min(BN, N - n_base);
+
+  // A: direct buffer -> LDS, 16 bytes per lane per instruction; an instruction
+  // fills 8 consecutive tile rows (lane i -> row i / 8, physical chunk i % 8),
+  // so the swizzle is applied to the source offsets.
+  const rsrc_t ra = make_rsrc(A + (int64_t)m_base * K, (int64_t)rows_m * K * 2);
+  int a_off[WROWS / 8];
+#pragma unroll
+  for (int s = 0; s < WROWS / 8; ++s) {
+    const int r = wave * WROWS + s * 8 + (lane >> 3);
+    a_off[s] = r * K * 2 + swz(r, lane & 7) * 16;
+  }
+  auto load_a = [&](int k0, uint4* buf) {
+#pragma unroll
+    for (int s = 0; s < WROWS / 8; ++s) {
+      uint4* dst = buf + (wave * WROWS + s * 8) * 8;
+      buffer_load_lds16(ra, dst, a_off[s], k0 * 2);
+    }
+  };
+
+  // B: the lane's weight rows within the tile
+  const rsrc_t rc = make_rsrc(codes + (int64_t)n_base * (K / 8), (int64_t)rows_n * (K / 2));
+  constexpr int gsz = (DEC == DEC_AFFINE) ? 64 : (DEC == DEC_MXFP4) ? 32 : 16;
+  constexpr int sbytes = (DEC == DEC_AFFINE) ? 2 : 1;
+  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) +
+                                  (int64_t)n_base * (K / gsz) * sbytes,
+                              (int64_t)rows_n * (K / gsz) * sbytes);
+  const rsrc_t rb = make_rsrc(biases ? biases + (int64_t)n_base * (K / 64) : nullptr,
+                              biases ? (int64_t)rows_n * (K / 64) * 2 : 0);
+  int nl[WNT];
+#pragma unroll
+  for (int j = 0; j < WNT; ++j) nl[j] = wn * 32 * WNT + 32 * j + l32;
+  auto load_b = [&](int k0, BFrag (&dst)[WNT]) {
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) load_bfrag_buf<DEC>(dst[j], rc, rs, rb, nl[j], K, k0, h);
+  };
+
+  f32x16_t acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // One K step: wait until every wave's loads for this step have landed,
+  // issue the next step's loads into the other buffer, then run the MFMAs.
+  auto step = [&](int k0, uint4* cur_lds, uint4* nxt_lds, BFrag (&cur)[WNT],
+                  BFrag (&nxt)[WNT]) {
+    wait_vmem();
+    __syncthreads();
+    if (k0 + 64 < K) {
+      load_a(k0 + 64, nxt_lds);
+      load_b(k0 + 64, nxt);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 a[WMT];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int r = wm * 32 * WMT + 32 * i + l32;
+        a[i] = cur_lds[r * 8 + swz(r, 4 * h + kk)];
+      }
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const Op8 b = expand<DEC>(cur[j], kk);
+#pragma unroll
+        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], b, acc[i][j]);
+      }
+    }
+  };
+
+  BFrag b0[WNT], b1[WNT];
+  load_a(0, lds0);
+  load_b(0, b0);
+  for (int k0 = 0; k0 < K; k0 += 128) {
+    step(k0, lds0, lds1, b0, b1);
+    if (k0 + 64 < K) step(k0 + 64, lds1, lds0, b1, b0);
+  }
+
+  const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
+  const bool full = (rows_m == BM) && (rows_n == BN);
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int n = n_base + wn * 32 * WNT + 32 * j + l32;
+      const int m0 = m_base + wm * 32 * WMT + 32 * i + 4 * h;
+      uint16_t* yp = Y + (int64_t)m0 * N + n;
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 8 * (r >> 2) + (r & 3);
+          if (m < M && n < N)
+            yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+        }
+      }
+    }
+}
+
+// MXFP4 x MXFP4 on the block-scaled MFMA.  Operands come straight from the
+// packed codes in global memory (L2-resident across the tiles that share
+// them), one K step (64) ahead.
+template <int WMT, int WNT>
+__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
+    const uint32_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+    const uint32_t* __restrict__ wc, const uint8_t* __restrict__ wsc, int M, int N, int K,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * 64 * WMT + wm * 32 * WMT, n0 = tn * 64 * WNT + wn * 32 * WNT;
+
+  int64_t mr[WMT], nr[WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i) mr[i] = min(m0 + 32 * i + l32, M - 1);
+#pragma unroll
+  for (int j = 0; j < WNT; ++j) nr[j] = min(n0 + 32 * j + l32, N - 1);
+
+  uint4 an[WMT], bn[WNT];
+  uint32_t asn[WMT], bsn[WNT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      an[i] = *reinterpret_cast<const uint4*>(xc + mr[i] * (K / 8) + k0 / 8 + 4 * h);
+      asn[i] = xs[mr[i] * (K / 32) + k0 / 32 + h];
+    }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      bn[j] = *reinterpret_cast<const uint4*>(wc + nr[j] * (K / 8) + k0 / 8 + 4 * h);
+      bsn[j] = wsc[nr[j] * (K / 32) + k0 / 32 + h];
+    }
+  };
+
+  f32x16_t acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    uint4 ac[WMT], bc[WNT];
+    uint32_t asc[WMT], bsc[WNT];
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) { ac[i] = an[i]; asc[i] = asn[i]; }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) { bc[j] = bn[j]; bsc[j] = bsn[j]; }
+    if (k0 + 64 < K) load(k0 + 64);
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      const i32x8_t av = {(int)ac[i].x, (int)ac[i].y, (int)ac[i].z, (int)ac[i].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const i32x8_t bv = {(int)bc[j].x, (int)bc[j].y, (int)bc[j].z, (int)bc[j].w, 0, 0, 0, 0};
+        // formats 4/4: FP4 E2M1 for both operands; scales: E8M0 byte 0
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            av, bv, acc[i][j], 4, 4, 0, (int)asc[i], 0, (int)bsc[j]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int n = n0 + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+      }
+    }
+}
+
+template <int DEC, int WGM, int WGN, int WMT, int WNT>
+hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
+                  const float* g2, uint16_t* y, hipStream_t s) {
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>), dim3(tiles_m * tiles_n),
+                     dim3(64 * WGM * WGN), 0, s, A, w.codes, w.scales, w.biases, g1, g2, M, N,
+                     K, y, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// Tile shapes: 256 x 256 with 8 waves (each 128 x 64) for prefill row
+// counts; narrower M tiles for small M.
+template <int DEC>
+hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
+                    const float* g2, uint16_t* y, hipStream_t s) {
+  if (M <= 64) return run_dq<DEC, 1, 4, 2, 2>(A, M, w, g1, g2, y, s);
+  if (M <= 128) return run_dq<DEC, 2, 4, 2, 2>(A, M, w, g1, g2, y, s);
+  return run_dq<DEC, 2, 4, 4, 2>(A, M, w, g1, g2, y, s);
+}
+
+hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,
+                  uint16_t* y, hipStream_t s) {
+  constexpr int WMT = 1, WNT = 1;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
+  const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
+  hipLaunchKernelGGL((gemm_mx_kernel<WMT, WNT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
+                     xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// Workspace for the qq paths:
+//   NVFP4: [amax f32, g_x f32] (256 B) + xhat fp16 [M, K]
+//   MXFP4: x codes uint32 [M, K/8] + x scales uint8 [M, K/32]
+size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act) {
+  if (act != BSFP_ACT_SAME) return 0;
+  if (mode == BSFP_NVFP4) return 256 + align256((size_t)M * K * 2);
+  if (mode == BSFP_MXFP4) return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+  return 0;
+}
+
+hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int act, void* ws,
+                      uint16_t* y, hipStream_t s) {
+  const int M = (int)M64;
+  if (act == BSFP_ACT_BF16) {
+    switch (w.mode) {
+      case BSFP_AFFINE: return run_dq_m<DEC_AFFINE>(x, M, w, nullptr, nullptr, y, s);
+      case BSFP_MXFP4: return run_dq_m<DEC_MXFP4>(x, M, w, nullptr, nullptr, y, s);
+      default: return run_dq_m<DEC_NVFP4>(x, M, w, w.global_scale, nullptr, y, s);
+    }
+  }
+  const int64_t n = M64 * w.cols;
+  if (w.mode == BSFP_NVFP4) {
+    float* amax = reinterpret_cast<float*>(ws);
+    float* gx = amax + 1;
+    uint16_t* xhat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + 256);
+    hipError_t e = hipSuccess;
+    if (w.global_scale) {  // alpha = g_x * g_w with g_x = amax_x / 2688
+      e = launch_amax(x, n, amax, s);
+      if (e == hipSuccess) e = launch_quantize_dequant_nvfp4_f16(x, n / 8, xhat, amax, 1, gx, s);
+      if (e != hipSuccess) return e;
+      return run_dq_m<DEC_NVFP4_F16>(xhat, M, w, gx, w.global_scale, y, s);
+    }
+    e = launch_quantize_dequant_nvfp4_f16(x, n / 8, xhat, nullptr, 0, nullptr, s);
+    if (e != hipSuccess) return e;
+    return run_dq_m<DEC_NVFP4_F16>(xhat, M, w, nullptr, nullptr, y, s);
+  }
+  // MXFP4
+  uint32_t* xc = reinterpret_cast<uint32_t*>(ws);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws) + align256((size_t)n / 2);
+  hipError_t e = launch_quantize_mxfp4(x, n / 8, xc, xs, s);
+  if (e != hipSuccess) return e;
+  return run_mx(xc, xs, M, w, y, s);
+}
+
+}  // namespace bsfp

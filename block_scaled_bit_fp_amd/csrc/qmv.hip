@@ -38,7 +38,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTeam = 32;                 // lanes per weight row
 constexpr int kTeams = kThreads / kTeam;  // rows in flight per workgroup
-constexpr int kPrefetch = 8;              // chunk loads in flight per lane
+constexpr int kPrefetch = 4;              // chunk loads in flight per lane
 constexpr int kLdsBudget = 53 * 1024;     // three workgroups per CU (160 KB LDS)
 
 // LDS layout for one K slice of ks elements (nch = ks / 32 chunks):
@@ -151,8 +151,10 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
         if constexpr (MODE == BSFP_MXFP4) {
           acc[m] = __builtin_fmaf(D0 + D1, e8m0_decode(it.s), acc[m]);
         } else {
-          acc[m] = __builtin_fmaf(D0, e4m3_decode(it.s & 0xFFu), acc[m]);
-          acc[m] = __builtin_fmaf(D1, e4m3_decode(it.s >> 8), acc[m]);
+          // both E4M3 block scales with the hardware converter (exact)
+          const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(it.s, 1.0f, false);
+          acc[m] = __builtin_fmaf(D0, sc.x, acc[m]);
+          acc[m] = __builtin_fmaf(D1, sc.y, acc[m]);
         }
       }
     }
