@@ -83,11 +83,17 @@ def _check(status: int):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream():
-    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    """The current HIP stream of the current device, as a raw pointer."""
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def version() -> str:
@@ -111,11 +117,15 @@ class QuantizedTensor:
         return GROUP[self.mode]
 
     def desc(self) -> QTensorDesc:
-        return QTensorDesc(self.mode, 4, GROUP[self.mode], self.rows, self.cols,
-                           self.codes.data_ptr(), self.scales.data_ptr(),
-                           None if self.biases is None else self.biases.data_ptr(),
-                           None if self.global_scale is None else self.global_scale.data_ptr(),
-                           None if self.amax is None else self.amax.data_ptr())
+        """The C descriptor; rebuilt whenever a field or a tensor's storage changed."""
+        ts = (self.codes, self.scales, self.biases, self.global_scale, self.amax)
+        key = (self.mode, self.rows, self.cols) + tuple(
+            None if t is None else t.data_ptr() for t in ts)
+        cached = self.__dict__.get("_desc")
+        if cached is None or cached[0] != key:
+            d = QTensorDesc(self.mode, 4, GROUP[self.mode], self.rows, self.cols, *key[3:])
+            self.__dict__["_desc"] = cached = (key, d)
+        return cached[1]
 
 
 def empty_quantized(mode: int, rows: int, cols: int, device="cuda",

@@ -87,6 +87,7 @@ bsfp_status check_qtensor(const bsfp_qtensor* q, const char* fn) {
 
 std::mutex g_cu_mutex;
 int g_cu_count[64] = {0};
+int g_max_lds[64] = {0};
 
 }  // namespace
 
@@ -102,6 +103,20 @@ int device_cu_count() {
     g_cu_count[dev] = n;
   }
   return g_cu_count[dev];
+}
+
+int device_max_lds() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_max_lds[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        n <= 0)
+      n = 64 * 1024;
+    g_max_lds[dev] = n;
+  }
+  return g_max_lds[dev];
 }
 
 }  // namespace bsfp

@@ -141,4 +141,38 @@ __device__ __forceinline__ float team_sum(float v) {
   return v;
 }
 
+// Sum over the 32 lanes of each half-wave, result in every lane: two
+// quad_perm exchanges, row_half_mirror and row_mirror on the DPP path (no
+// LDS), then one ds_swizzle xor 16 between the two 16-lane rows.
+__device__ __forceinline__ float dpp_sum32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return v;
+}
+
+// ---------------------------------------------------------------- buffers
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes), bytes < 2^32: 32-bit
+// offsets, and a load whose per-lane offset lies past the end returns 0.
+constexpr int kRawBufferFlags = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(uint32_t)bytes, kRawBufferFlags);
+}
+
+__device__ __forceinline__ uint4 buffer_load_u128(rsrc_t r, int voff, int soff) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
+// including the direct-to-LDS ones the compiler does not track.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace bsfp

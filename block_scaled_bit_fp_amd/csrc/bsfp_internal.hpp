@@ -13,6 +13,8 @@ namespace bsfp {
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+// Largest LDS allocation one workgroup may make on the current device.
+int device_max_lds();
 
 // ---- amax / quantize / dequantize (quantize.hip)
 hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_t s);

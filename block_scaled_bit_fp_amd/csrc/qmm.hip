@@ -147,16 +147,6 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor over [base, base + bytes): 32-bit offsets, loads past
-// the end return 0 (rows beyond M or N read as zeros).
-constexpr int kRawBufferFlags = 0x00020000;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                           (int)(uint32_t)bytes, kRawBufferFlags);
-}
 
 // 16 bytes per lane from a buffer straight into LDS: the LDS base is
 // wave-uniform and lane i lands at base + 16 i.  (Kept out of line of the
@@ -165,10 +155,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
-
-// s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
-// including the direct-to-LDS ones the compiler does not track.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Physical 16-byte chunk of logical chunk c in tile row r.  The XOR with r & 7
 // spreads 8 consecutive rows over the 8 chunks of a 128-byte row; the extra

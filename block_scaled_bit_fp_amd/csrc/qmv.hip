@@ -28,6 +28,8 @@
 // and u = (w >> 4) & 0x0F0F0F0F the four converted pairs are (q0,q2),
 // (q4,q6), (q1,q3), (q5,q7); x is staged in that pair order.  FP4 decode uses
 // v_cvt_scalef32_pk_bf16_fp4 (exact, unit scale) with x in natural order.
+#include <algorithm>
+
 #include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
 
@@ -267,6 +269,347 @@ __global__ __launch_bounds__(kThreads) void qmv_nvfp4_words_kernel(
   }
 }
 
+// ------------------------------------------------------------------ fast path
+//
+// Chunk c of a row (32 codes, 16 bytes) always goes to lane c % 32 of the
+// row's team, so a lane works on the same x chunks for every row it visits.
+// A wave owns blocks of 2R consecutive rows (team h takes rows 2r + h of the
+// block) and walks them chunk step by chunk step: step j loads chunk
+// 32 j + lt of each of its R rows, so the x values of one step are read from
+// LDS once and used for R rows.  All addresses are per-lane constants plus
+// wave-uniform offsets (raw buffer loads: descriptor at the block's first row,
+// 32-bit lane offset, scalar step offset); rows past N fall outside the
+// descriptor and read as zeros.  kRing chunk loads per lane stay in flight,
+// and the pipeline runs across row blocks.
+constexpr int kRing = 8;
+
+struct Chunk {
+  uint4 w;     // 32 codes
+  uint32_t s;  // scale bits
+  uint32_t b;  // affine bias bits
+};
+
+// LDS bytes of the staged activations: x units [M][NJ][4][32] of 16 bytes,
+// plus (affine) the per-chunk sums of x [M][NJ][32] for the bias term.
+template <int MODE>
+size_t fast_lds_bytes(int M, int NJ) {
+  return (size_t)M * NJ * (2048 + (MODE == BSFP_AFFINE ? 128 : 0));
+}
+
+// Staging of x for the fast kernel, split in two so that the x loads can go
+// out before the first weight loads and the LDS writes wait only for them.
+// Unit (m, c, u) holds x[m, 32c + 8u .. + 7] (affine: pairs reordered as the
+// nibble decode produces them); chunks past the row end are zero, so they
+// contribute nothing.  Each thread owns units tid + i * blockDim, i < kXU.
+constexpr int kXU = 8;
+
+__device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int M, int K,
+                                             int NJ, uint4 (&xr)[kXU]) {
+  const int cpr = K / 32;
+  const int units = M * NJ * 128;
+#pragma unroll
+  for (int i = 0; i < kXU; ++i) {
+    const int b = threadIdx.x + i * blockDim.x;
+    xr[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (b < units) {
+      const int m = b / (NJ * 128);
+      const int rem = b - m * NJ * 128;
+      const int c = rem >> 2, u = rem & 3;
+      if (c < cpr) xr[i] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * c + 8 * u);
+    }
+  }
+}
+
+template <bool AFF>
+__device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[kXU],
+                                              uint4* __restrict__ xp, float* __restrict__ xs) {
+  const int units = M * NJ * 128;
+#pragma unroll
+  for (int i = 0; i < kXU; ++i) {
+    const int b = threadIdx.x + i * blockDim.x;
+    if (b < units) {  // units % 4 == 0: the 4 threads of a chunk agree
+      const int m = b / (NJ * 128);
+      const int rem = b - m * NJ * 128;
+      const int c = rem >> 2, u = rem & 3;
+      const uint4 v = xr[i];
+      uint4 o = v;
+      if constexpr (AFF) {
+        o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
+        o.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (x4, x6)
+        o.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
+        o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (x5, x7)
+        float t = bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) +
+                  bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+        t = team_sum<4>(t);  // the 4 units of chunk c are 4 adjacent threads
+        if (u == 0) xs[(m * NJ + (c >> 5)) * 32 + (c & 31)] = t;
+      }
+      xp[((m * NJ + (c >> 5)) * 4 + u) * 32 + (c & 31)] = o;
+    }
+  }
+}
+
+// Bytes of the per-wave scale staging area of one block of 2R rows
+// (scales, then affine biases).
+template <int MODE>
+int block_scale_bytes(int R, int K) {
+  const int gs = MODE == BSFP_AFFINE ? 64 : MODE == BSFP_MXFP4 ? 32 : 16;
+  const int srb = (K / gs) * (MODE == BSFP_AFFINE ? 2 : 1);
+  return 2 * R * srb * (MODE == BSFP_AFFINE ? 2 : 1);
+}
+constexpr int kScaleLoads = 4;  // 16-byte scale loads per lane and array, at most
+
+// MAXM: compile-time bound on M.  R: rows per team per block.
+// RAGGED: the row length in chunks is not a multiple of 32, so some lanes
+//   have no chunk in the last step; their scale and bias are forced to zero
+//   (x is zero there already) so a NaN or Inf scale of the next row cannot
+//   leak in.
+// SLDS: the block's scales (2R rows, contiguous) are fetched with 16-byte
+//   loads when its first step is fetched, written to a per-wave LDS area when
+//   that step is consumed, and read from there per chunk -- instead of one
+//   1- or 2-byte load per chunk.  Needs a whole number of 16-byte pieces per
+//   row, at most kScaleLoads loads per lane, and PJ <= NJ, so that the next
+//   block's scales are fetched only after this block's are in LDS.
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
+__global__ __launch_bounds__(1024) void qmv_fast_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
+    const void* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const float* __restrict__ gptr, uint16_t* __restrict__ y, int NJ, int nblocks) {
+  static_assert(!(SLDS && RAGGED), "staged scales need whole 32-chunk steps");
+  constexpr bool AFF = (MODE == BSFP_AFFINE);
+  constexpr int PJ = kRing / R;  // steps in flight
+  constexpr int gs = AFF ? 64 : (MODE == BSFP_MXFP4) ? 32 : 16;
+  constexpr int sbytes = AFF ? 2 : 1;
+  constexpr int sstep = 32 * 32 / gs * sbytes;  // scale bytes of one step (32 chunks)
+  extern __shared__ uint4 smem[];
+  uint4* xp = smem;
+  float* xs = reinterpret_cast<float*>(smem + M * NJ * 128);
+
+  const int lane = threadIdx.x & 63, h = lane >> 5, lt = lane & 31;
+  const int wpg = blockDim.x >> 6;
+  const int wave_in_wg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int cpr = K >> 5;
+  const int rb = K >> 1;              // code bytes per row
+  const int srb = (K / gs) * sbytes;  // scale bytes per row
+  // Blocks are dealt round-robin over the workgroups (one per CU), then over
+  // the waves of a workgroup: pass p of this wave takes block
+  // (p * wpg + wave_in_wg) * G + wg, so no CU has more than one extra block.
+  const int nb_wg = nblocks > wg ? (nblocks - wg + G - 1) / G : 0;
+  const int passes = wave_in_wg < nb_wg ? (nb_wg - wave_in_wg + wpg - 1) / wpg : 0;
+  const int steps = passes * NJ;
+  const float g = (MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f;
+
+  // this wave's scale area (SLDS): [2R rows][srb] scales, then the biases
+  const int sarea = 2 * R * srb;
+  uint8_t* sl = reinterpret_cast<uint8_t*>(
+      smem + (M * NJ * (AFF ? 136 : 128))) + wave_in_wg * (AFF ? 2 : 1) * sarea;
+  const int nsl = (sarea + 1023) >> 10;  // 16-byte scale loads per lane and array
+
+  int vc[R], vs[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    vc[r] = (2 * r + h) * rb + 16 * lt;
+    vs[r] = (2 * r + h) * srb + (AFF ? 2 * (lt >> 1) : (MODE == BSFP_MXFP4) ? lt : 2 * lt);
+  }
+
+  rsrc_t rc, rs, rbs;
+  auto block_row0 = [&](int p) -> int64_t {
+    return ((int64_t)(p * wpg + wave_in_wg) * G + wg) * (2 * R);
+  };
+  auto set_block = [&](int p) {
+    const int64_t row0 = block_row0(p);
+    const int64_t rows = min((int64_t)N - row0, (int64_t)(2 * R));
+    rc = make_rsrc(reinterpret_cast<const uint8_t*>(codes) + row0 * rb, rows * rb);
+    rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + row0 * srb, rows * srb);
+    if constexpr (AFF)
+      rbs = make_rsrc(reinterpret_cast<const uint8_t*>(biases) + row0 * srb, rows * srb);
+  };
+  uint4 sreg[SLDS ? kScaleLoads : 1], breg[SLDS && AFF ? kScaleLoads : 1];
+  auto fetch = [&](Chunk (&dst)[R], int j) {
+    if constexpr (SLDS) {
+      if (j == 0) {  // the block's scales, 16 bytes per lane and load
+#pragma unroll
+        for (int i = 0; i < kScaleLoads; ++i) {
+          if (i < nsl) {
+            sreg[i] = buffer_load_u128(rs, 16 * lane, i * 1024);
+            if constexpr (AFF) breg[i] = buffer_load_u128(rbs, 16 * lane, i * 1024);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      dst[r].w = buffer_load_u128(rc, vc[r], j * 512);
+      if constexpr (!SLDS) {
+        if constexpr (AFF) {
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 0);
+          dst[r].b = __builtin_amdgcn_raw_buffer_load_b16(rbs, vs[r], j * sstep, 0);
+        } else if constexpr (MODE == BSFP_MXFP4) {
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b8(rs, vs[r], j * sstep, 0);
+        } else {
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 0);
+        }
+      }
+    }
+  };
+
+  float acc[R][MAXM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[r][m] = 0.0f;
+
+  // x loads first, then the first PJ steps of weights; staging x into LDS
+  // then waits only for the x loads (loads complete in issue order).
+  uint4 xr[kXU];
+  stage_x_load(x, M, K, NJ, xr);
+  Chunk ring[PJ][R];
+  int pf = 0, jf = 0;  // next step to fetch
+  if (steps > 0) {
+    set_block(0);
+#pragma unroll
+    for (int u = 0; u < PJ; ++u) {
+      fetch(ring[u], pf < passes ? jf : NJ - 1);
+      if (pf < passes && ++jf == NJ) {
+        jf = 0;
+        if (++pf < passes) set_block(pf);
+      }
+    }
+  }
+  stage_x_store<AFF>(M, NJ, xr, xp, xs);
+  __syncthreads();
+  if (steps == 0) return;
+
+  int pc = 0, jc = 0;  // next step to consume
+  for (int s0 = 0; s0 < steps; s0 += PJ) {
+#pragma unroll
+    for (int u = 0; u < PJ; ++u) {
+      if (s0 + u < steps) {
+        if constexpr (SLDS) {
+          if (jc == 0) {  // this block's scales into the wave's LDS area
+#pragma unroll
+            for (int i = 0; i < kScaleLoads; ++i) {
+              if (i < nsl) {
+                if (16 * (lane + 64 * i) < sarea) {
+                  *reinterpret_cast<uint4*>(sl + 16 * (lane + 64 * i)) = sreg[i];
+                  if constexpr (AFF)
+                    *reinterpret_cast<uint4*>(sl + sarea + 16 * (lane + 64 * i)) = breg[i];
+                }
+              }
+            }
+          }
+        }
+        const bool valid = !RAGGED || (32 * jc + lt < cpr);
+        uint32_t sv[R], bv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if constexpr (SLDS) {
+            const uint8_t* sp = sl + vs[r] + jc * sstep;
+            if constexpr (AFF) {
+              sv[r] = *reinterpret_cast<const uint16_t*>(sp);
+              bv[r] = *reinterpret_cast<const uint16_t*>(sp + sarea);
+            } else if constexpr (MODE == BSFP_MXFP4) {
+              sv[r] = *sp;
+            } else {
+              sv[r] = *reinterpret_cast<const uint16_t*>(sp);
+            }
+          } else {
+            sv[r] = valid ? ring[u][r].s : 0u;
+            bv[r] = valid ? ring[u][r].b : 0u;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+          if (MAXM > 1 && m >= M) break;
+          const uint4* xq = xp + (m * NJ + jc) * 128 + lt;
+          const uint4 x0 = xq[0], x1 = xq[32], x2 = xq[64], x3 = xq[96];
+          const float xsum = AFF ? xs[(m * NJ + jc) * 32 + lt] : 0.0f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint4 w = ring[u][r].w;
+            if constexpr (AFF) {
+              float D0 = 0.0f, D1 = 0.0f;
+              uint32_t t = w.x & 0x0F0F0F0Fu, q = (w.x >> 4) & 0x0F0F0F0Fu;
+              D0 = dot2_bf16(x0.x, nibbles_to_bf16x2<false>(t), D0);
+              D0 = dot2_bf16(x0.y, nibbles_to_bf16x2<true>(t), D0);
+              D0 = dot2_bf16(x0.z, nibbles_to_bf16x2<false>(q), D0);
+              D0 = dot2_bf16(x0.w, nibbles_to_bf16x2<true>(q), D0);
+              t = w.y & 0x0F0F0F0Fu, q = (w.y >> 4) & 0x0F0F0F0Fu;
+              D1 = dot2_bf16(x1.x, nibbles_to_bf16x2<false>(t), D1);
+              D1 = dot2_bf16(x1.y, nibbles_to_bf16x2<true>(t), D1);
+              D1 = dot2_bf16(x1.z, nibbles_to_bf16x2<false>(q), D1);
+              D1 = dot2_bf16(x1.w, nibbles_to_bf16x2<true>(q), D1);
+              t = w.z & 0x0F0F0F0Fu, q = (w.z >> 4) & 0x0F0F0F0Fu;
+              D0 = dot2_bf16(x2.x, nibbles_to_bf16x2<false>(t), D0);
+              D0 = dot2_bf16(x2.y, nibbles_to_bf16x2<true>(t), D0);
+              D0 = dot2_bf16(x2.z, nibbles_to_bf16x2<false>(q), D0);
+              D0 = dot2_bf16(x2.w, nibbles_to_bf16x2<true>(q), D0);
+              t = w.w & 0x0F0F0F0Fu, q = (w.w >> 4) & 0x0F0F0F0Fu;
+              D1 = dot2_bf16(x3.x, nibbles_to_bf16x2<false>(t), D1);
+              D1 = dot2_bf16(x3.y, nibbles_to_bf16x2<true>(t), D1);
+              D1 = dot2_bf16(x3.z, nibbles_to_bf16x2<false>(q), D1);
+              D1 = dot2_bf16(x3.w, nibbles_to_bf16x2<true>(q), D1);
+              acc[r][m] = __builtin_fmaf(__uint_as_float(sv[r] << 16), D0 + D1, acc[r][m]);
+              acc[r][m] = __builtin_fmaf(__uint_as_float(bv[r] << 16), xsum, acc[r][m]);
+            } else {
+              float D0 = 0.0f, D1 = 0.0f;
+              D0 = dot2_bf16(x0.x, e2m1x2_to_bf16x2<0>(w.x), D0);
+              D0 = dot2_bf16(x0.y, e2m1x2_to_bf16x2<1>(w.x), D0);
+              D0 = dot2_bf16(x0.z, e2m1x2_to_bf16x2<2>(w.x), D0);
+              D0 = dot2_bf16(x0.w, e2m1x2_to_bf16x2<3>(w.x), D0);
+              D0 = dot2_bf16(x1.x, e2m1x2_to_bf16x2<0>(w.y), D0);
+              D0 = dot2_bf16(x1.y, e2m1x2_to_bf16x2<1>(w.y), D0);
+              D0 = dot2_bf16(x1.z, e2m1x2_to_bf16x2<2>(w.y), D0);
+              D0 = dot2_bf16(x1.w, e2m1x2_to_bf16x2<3>(w.y), D0);
+              D1 = dot2_bf16(x2.x, e2m1x2_to_bf16x2<0>(w.z), D1);
+              D1 = dot2_bf16(x2.y, e2m1x2_to_bf16x2<1>(w.z), D1);
+              D1 = dot2_bf16(x2.z, e2m1x2_to_bf16x2<2>(w.z), D1);
+              D1 = dot2_bf16(x2.w, e2m1x2_to_bf16x2<3>(w.z), D1);
+              D1 = dot2_bf16(x3.x, e2m1x2_to_bf16x2<0>(w.w), D1);
+              D1 = dot2_bf16(x3.y, e2m1x2_to_bf16x2<1>(w.w), D1);
+              D1 = dot2_bf16(x3.z, e2m1x2_to_bf16x2<2>(w.w), D1);
+              D1 = dot2_bf16(x3.w, e2m1x2_to_bf16x2<3>(w.w), D1);
+              if constexpr (MODE == BSFP_MXFP4) {
+                acc[r][m] = __builtin_fmaf(D0 + D1, e8m0_decode(sv[r]), acc[r][m]);
+              } else {
+                // both E4M3 block scales with the hardware converter (exact)
+                const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sv[r], 1.0f, false);
+                acc[r][m] = __builtin_fmaf(D0, sc.x, acc[r][m]);
+                acc[r][m] = __builtin_fmaf(D1, sc.y, acc[r][m]);
+              }
+            }
+          }
+        }
+        if (jc == NJ - 1) {  // the block's rows are complete
+          const int64_t row0 = block_row0(pc);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int64_t row = row0 + 2 * r + h;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+              if (MAXM > 1 && m >= M) break;
+              const float v = dpp_sum32(acc[r][m]);
+              if (lt == 0 && row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16(v * g);
+              acc[r][m] = 0.0f;
+            }
+          }
+        }
+        if (++jc == NJ) {
+          jc = 0;
+          ++pc;
+        }
+      }
+      // refill this slot with step s0 + u + PJ (past the end: reload the last
+      // step, whose data is never consumed)
+      fetch(ring[u], pf < passes ? jf : NJ - 1);
+      if (pf < passes && ++jf == NJ) {
+        jf = 0;
+        if (++pf < passes) set_block(pf);
+      }
+    }
+  }
+}
+
 template <int MODE, int MAXM>
 size_t lds_bytes(int64_t k) {
   return (size_t)k * 2 * MAXM + (MODE == BSFP_AFFINE ? (size_t)(k / 64) * 4 * MAXM : 0);
@@ -294,8 +637,103 @@ hipError_t run(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hip
   return hipGetLastError();
 }
 
+// Launch shape of the fast kernel: one workgroup per CU (its LDS request is
+// raised above half of the CU's LDS when needed, so two never share a CU),
+// with as many waves (at most 16) as it takes to hold every block in one
+// pass, or in as few passes as possible; at least enough waves to stage x.
+struct FastShape {
+  int grid, wpg;
+  size_t lds;
+};
+
+template <int MODE, int R, bool SLDS>
+FastShape fast_shape(int M, int K, int NJ, int64_t N) {
+  const int cus = device_cu_count();
+  const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
+  const int units = M * NJ * 128;
+  const int min_wpg = std::max(1, (units + kXU * 64 - 1) / (kXU * 64));
+  const int64_t grid = std::min<int64_t>(cus, nblocks);
+  const int64_t passes = std::max<int64_t>(1, (nblocks + grid * 16 - 1) / (grid * 16));
+  const int wpg = (int)std::min<int64_t>(
+      16, std::max<int64_t>(min_wpg, (nblocks + grid * passes - 1) / (grid * passes)));
+  size_t lds = fast_lds_bytes<MODE>(M, NJ) +
+               (SLDS ? (size_t)wpg * block_scale_bytes<MODE>(R, K) : 0);
+  const size_t half = (size_t)device_max_lds() / 2 + 16;
+  if (grid == cus && wpg <= 8 && lds < half) lds = half;
+  return FastShape{(int)grid, wpg, lds};
+}
+
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
+hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, int NJ,
+                       hipStream_t s) {
+  const int64_t N = w.rows;
+  const int K = (int)w.cols;
+  const FastShape sh = fast_shape<MODE, R, SLDS>(M, K, NJ, N);
+  const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
+  if (sh.lds > 64 * 1024) {  // opt in to the large LDS allocation (160 KB on gfx950)
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>), dim3((unsigned)sh.grid),
+                     dim3(64 * sh.wpg), sh.lds, s, x, M, K, (int)N, w.codes, w.scales,
+                     w.biases, w.global_scale, y, NJ, (int)nblocks);
+  return hipGetLastError();
+}
+
+// The staged x (kXU units per thread) is limited to 64 KB; the per-wave
+// scale areas come on top, up to the device's per-workgroup LDS limit.
+constexpr size_t kFastXLdsMax = 64 * 1024;
+
+template <int MODE>
+bool fast_ok(int M, int NJ) {
+  return (size_t)M * NJ * 2048 <= kFastXLdsMax &&
+         fast_lds_bytes<MODE>(M, NJ) <= (size_t)device_max_lds();
+}
+
+// Staged scales apply when every row holds whole 32-chunk steps and whole
+// 16-byte scale pieces, the block's scales fit kScaleLoads loads per lane,
+// at most NJ steps are in flight, and the LDS fits.
+template <int MODE, int R>
+bool slds_ok(int K, int NJ, int M, int64_t N) {
+  const int cpr = K / 32;
+  const int sarea = block_scale_bytes<MODE>(R, K) / (MODE == BSFP_AFFINE ? 2 : 1);
+  const int srb = sarea / (2 * R);
+  if (cpr % 32 || srb % 16 || sarea > kScaleLoads * 1024 || kRing / R > NJ) return false;
+  return fast_shape<MODE, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
+}
+
 template <int MODE>
 hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hipStream_t s) {
+  const int K = (int)w.cols;
+  const int NJ = (int)((w.cols / 32 + 31) / 32);
+  const bool ragged = (w.cols / 32) % 32 != 0;
+  if (fast_ok<MODE>(M, NJ) && w.cols < (1 << 28) && w.rows < (1 << 30)) {
+    if (M == 1) {
+      // the largest block (rows per team) that still gives every CU 8 waves
+      const int64_t want = 8LL * device_cu_count();
+      const int64_t N = w.rows;
+      if (N >= 8 * want && slds_ok<MODE, 4>(K, NJ, M, N))
+        return launch_fast<MODE, 1, 4, false, true>(x, M, w, y, NJ, s);
+      if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, M, N))
+        return launch_fast<MODE, 1, 2, false, true>(x, M, w, y, NJ, s);
+      if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true>(x, M, w, y, NJ, s);
+      if (slds_ok<MODE, 2>(K, NJ, M, N)) return launch_fast<MODE, 1, 2, false, true>(x, M, w, y, NJ, s);
+      if (slds_ok<MODE, 4>(K, NJ, M, N)) return launch_fast<MODE, 1, 4, false, true>(x, M, w, y, NJ, s);
+      if (ragged) return launch_fast<MODE, 1, 1, true, false>(x, M, w, y, NJ, s);
+      return launch_fast<MODE, 1, 1, false, false>(x, M, w, y, NJ, s);
+    }
+    if (ragged) {
+      if (M == 2) return launch_fast<MODE, 2, 1, true, false>(x, M, w, y, NJ, s);
+      if (M <= 4) return launch_fast<MODE, 4, 1, true, false>(x, M, w, y, NJ, s);
+      return launch_fast<MODE, 8, 1, true, false>(x, M, w, y, NJ, s);
+    }
+    if (M == 2) return launch_fast<MODE, 2, 1, false, false>(x, M, w, y, NJ, s);
+    if (M <= 4) return launch_fast<MODE, 4, 1, false, false>(x, M, w, y, NJ, s);
+    return launch_fast<MODE, 8, 1, false, false>(x, M, w, y, NJ, s);
+  }
+  // x too large for one LDS copy: walk K in slices
   if (M == 1) return run<MODE, 1>(x, M, w, y, s);
   if (M == 2) return run<MODE, 2>(x, M, w, y, s);
   if (M <= 4) return run<MODE, 4>(x, M, w, y, s);
