@@ -138,6 +138,7 @@ def main():
         f"{sweep_bytes / 1e9:.2f} GB")
 
     # ------------------------------------------------------------- stages
+    stream = torch.cuda.current_stream()  # the library launches on this stream
     def st_act_quant():
         b.quantize(X_act, b.NVFP4, "compute", out=q_act)
 
@@ -148,8 +149,21 @@ def main():
         b.quantize(W_mx_bf, b.MXFP4, out=q_mx_out)
         b.quantize(W_small, b.AFFINE, out=q_small_out)
 
-    def st_qmv_sweep():
-        for x, q, y in sweep:
+    # Kernel-level timing of the sweep's GEMV: every 16th launch of a timed
+    # sweep carries a pair of HIP events that record that kernel's own start
+    # and end (bsfp_time_next_launch).  A timed launch costs a few us of extra
+    # queue latency, so only a sample is timed; 16 = 1 (mod 3) cycles the
+    # sample through the gate, up and down matrices.
+    SAMPLE = 16
+    hip = HipEvents((len(sweep) // SAMPLE + 1) * args.steps * 2)
+    launch_ev = []
+
+    def st_qmv_sweep(record=False):
+        for i, (x, q, y) in enumerate(sweep):
+            if record and i % SAMPLE == 0:
+                e0, e1 = hip.take(), hip.take()
+                b.time_next_launch(e0, e1)
+                launch_ev.append((q.rows, e0, e1))
             b.qmv(x, q, out=y)
 
     def st_qmv_fp4():
@@ -181,7 +195,6 @@ def main():
             stages.append(("copy", lambda: torch.bitwise_not(c_src, out=c_dst)))
     names = [n for n, _ in stages]
 
-    stream = torch.cuda.current_stream()
     ev = {n: [] for n in names}
 
     def step(record):
@@ -190,7 +203,7 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn()
+                fn(record=True) if n == "qmv_sweep" else fn()
                 e1.record(stream)
                 ev[n].append((e0, e1))
             else:
@@ -226,14 +239,26 @@ def main():
         out["value"] = round(gbs, 1)
         out["qmv_sweep_gbs"] = round(gbs, 1)
         per_launch = sweep_bytes / len(sweep)
-        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+        durs = {}
+        for rows, e0, e1 in launch_ev:
+            durs.setdefault(rows, []).append(hip.elapsed_ms(e0, e1))
+        all_ms = [d for v in durs.values() for d in v]
+        launch_ms = float(np.mean(all_ms))
+        kgbs = per_launch / (launch_ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic("qmv_affine_m1", ["qmv.hip"]),
-                           "kernel": "qmv_kernel<affine, M=1>",
+                           "kernel": "qmv_fast_kernel<affine, M=1>",
                            "bytes_per_launch": int(per_launch),
-                           "launch_us": round(ms["qmv_sweep"] * 1e3 / len(sweep), 3),
-                           "note": "average over the sweep's 192 back-to-back launches, "
-                                   "timed by one event pair on the launch stream"}
+                           "launch_us": round(launch_ms * 1e3, 3),
+                           "launch_us_by_shape": {
+                               ("[25600,5120]" if r == INTER else "[5120,25600]"):
+                                   round(float(np.mean(v)) * 1e3, 3) for r, v in durs.items()},
+                           "timed_launches": len(all_ms),
+                           "note": "algorithmic bytes of one launch / mean kernel duration "
+                                   "of every 16th launch of the timed sweeps (HIP start/stop "
+                                   "events attached to the GEMV launch); value is the whole "
+                                   "sweep including the gaps between launches"}
     if "qqmm" in ms:
         flop = 2.0 * 2048 * INTER * HIDDEN
         tfs = flop / (ms["qqmm"] * 1e-3) / 1e12
@@ -243,7 +268,9 @@ def main():
                                "frac": round(tfs / MFMA_F16_PEAK_TFS, 4),
                                "traffic": measured_traffic("qqmm_nvfp4_m2048", ["qmm.hip"]),
                                "kernel": "NVFP4 qqmm M=2048: amax + activation quantize "
-                                         "+ gemm_dq_kernel (fp16 MFMA)"}
+                                         "+ gemm_dq_kernel (fp16 MFMA)",
+                               "note": "whole bsfp_qmm call (three kernels) per event pair; "
+                                       "the GEMM kernel alone is in the kernel-trace summary"}
         for M in (1134, 4096):
             key = f"qqmm_{M}"
             if key in ms:
@@ -259,6 +286,37 @@ def main():
     if not args.no_cpu_baseline and out["value"] is not None:
         out["cpu_baseline"] = cpu_baseline(log)
     print(json.dumps(out), flush=True)
+
+
+class HipEvents:
+    """A pool of timing-enabled hipEvent_t handles from the HIP runtime that
+    PyTorch already loaded (plain handles for bsfp_time_next_launch)."""
+
+    def __init__(self, n):
+        import ctypes as C
+        self.C = C
+        self.rt = C.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.pool = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self.rt.hipEventCreate(C.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.pool.append(e.value)
+        self.next = 0
+
+    def take(self):
+        e = self.pool[self.next]
+        self.next += 1
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = self.C.c_float()
+        if self.rt.hipEventElapsedTime(self.C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
 
 
 def measured_traffic(name, sources):

@@ -29,7 +29,8 @@ ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
 
 EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
-           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_last_error", "bsfp_version")
+           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_time_next_launch",
+           "bsfp_last_error", "bsfp_version")
 
 
 class QTensorDesc(C.Structure):
@@ -66,6 +67,7 @@ def lib():
             "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
             "bsfp_qmm_workspace_bytes": (C.c_size_t, [I32, I64, I64, I32]),
             "bsfp_qmm": (C.c_int, [P, I64, QP, I32, P, C.c_size_t, P, P]),
+            "bsfp_time_next_launch": (C.c_int, [P, P]),
             "bsfp_last_error": (C.c_char_p, []),
             "bsfp_version": (C.c_char_p, []),
         }
@@ -94,6 +96,12 @@ def _stream():
     if _raw_stream is not None:
         return _raw_stream(torch.cuda.current_device())
     return torch.cuda.current_stream().cuda_stream
+
+
+def time_next_launch(start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """Attach two hipEvent_t handles (ints) to the main kernel of this thread's
+    next qmv / qmm call: they record that kernel's own start and end."""
+    _check(lib().bsfp_time_next_launch(start_event, stop_event))
 
 
 def version() -> str:

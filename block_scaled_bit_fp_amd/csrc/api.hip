@@ -105,6 +105,14 @@ int device_cu_count() {
   return g_cu_count[dev];
 }
 
+thread_local LaunchEvents g_launch_events = {nullptr, nullptr};
+
+LaunchEvents take_launch_events() {
+  const LaunchEvents e = g_launch_events;
+  g_launch_events = {nullptr, nullptr};
+  return e;
+}
+
 int device_max_lds() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
@@ -126,6 +134,11 @@ using namespace bsfp;
 extern "C" {
 
 const char* bsfp_last_error(void) { return g_err; }
+
+bsfp_status bsfp_time_next_launch(void* start_event, void* stop_event) {
+  g_launch_events = {(hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return BSFP_OK;
+}
 
 const char* bsfp_version(void) { return "bsfp 0.1.0 (gfx950)"; }
 

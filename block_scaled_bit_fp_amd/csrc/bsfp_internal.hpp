@@ -3,6 +3,7 @@
 // validated by the C-ABI layer (api.hip) and returns hipGetLastError().
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,6 +11,22 @@
 #include "../../include/bsfp.h"
 
 namespace bsfp {
+
+// The event pair set by bsfp_time_next_launch (cleared when taken).
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+LaunchEvents take_launch_events();
+
+// Launch of a main kernel: with the pending event pair when one is set.
+template <typename F, typename... Args>
+void launch_main(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
+  const LaunchEvents ev = take_launch_events();
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -393,7 +393,7 @@ hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* 
   const int N = (int)w.rows, K = (int)w.cols;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>), dim3(tiles_m * tiles_n),
+  launch_main(&gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>, dim3(tiles_m * tiles_n),
                      dim3(64 * WGM * WGN), 0, s, A, w.codes, w.scales, w.biases, g1, g2, M, N,
                      K, y, tiles_m, tiles_n);
   return hipGetLastError();
@@ -415,7 +415,7 @@ hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtens
   const int N = (int)w.rows, K = (int)w.cols;
   const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
   const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
-  hipLaunchKernelGGL((gemm_mx_kernel<WMT, WNT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
+  launch_main(&gemm_mx_kernel<WMT, WNT>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
                      xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m, tiles_n);
   return hipGetLastError();
 }

@@ -29,6 +29,7 @@
 // (q4,q6), (q1,q3), (q5,q7); x is staged in that pair order.  FP4 decode uses
 // v_cvt_scalef32_pk_bf16_fp4 (exact, unit scale) with x in natural order.
 #include <algorithm>
+#include <atomic>
 
 #include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
@@ -301,7 +302,7 @@ size_t fast_lds_bytes(int M, int NJ) {
 // Unit (m, c, u) holds x[m, 32c + 8u .. + 7] (affine: pairs reordered as the
 // nibble decode produces them); chunks past the row end are zero, so they
 // contribute nothing.  Each thread owns units tid + i * blockDim, i < kXU.
-constexpr int kXU = 8;
+constexpr int kXU = 4;
 
 __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int M, int K,
                                              int NJ, uint4 (&xr)[kXU]) {
@@ -356,7 +357,6 @@ int block_scale_bytes(int R, int K) {
   const int srb = (K / gs) * (MODE == BSFP_AFFINE ? 2 : 1);
   return 2 * R * srb * (MODE == BSFP_AFFINE ? 2 : 1);
 }
-constexpr int kScaleLoads = 4;  // 16-byte scale loads per lane and array, at most
 
 // MAXM: compile-time bound on M.  R: rows per team per block.
 // RAGGED: the row length in chunks is not a multiple of 32, so some lanes
@@ -367,7 +367,8 @@ constexpr int kScaleLoads = 4;  // 16-byte scale loads per lane and array, at mo
 //   loads when its first step is fetched, written to a per-wave LDS area when
 //   that step is consumed, and read from there per chunk -- instead of one
 //   1- or 2-byte load per chunk.  Needs a whole number of 16-byte pieces per
-//   row, at most kScaleLoads loads per lane, and PJ <= NJ, so that the next
+//   row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and PJ <= NJ,
+//   so that the next
 //   block's scales are fetched only after this block's are in LDS.
 template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
 __global__ __launch_bounds__(1024) void qmv_fast_kernel(
@@ -424,12 +425,13 @@ __global__ __launch_bounds__(1024) void qmv_fast_kernel(
     if constexpr (AFF)
       rbs = make_rsrc(reinterpret_cast<const uint8_t*>(biases) + row0 * srb, rows * srb);
   };
-  uint4 sreg[SLDS ? kScaleLoads : 1], breg[SLDS && AFF ? kScaleLoads : 1];
+  constexpr int SL = (MODE == BSFP_NVFP4) ? 4 : 2;
+  uint4 sreg[SLDS ? SL : 1], breg[SLDS && AFF ? SL : 1];
   auto fetch = [&](Chunk (&dst)[R], int j) {
     if constexpr (SLDS) {
       if (j == 0) {  // the block's scales, 16 bytes per lane and load
 #pragma unroll
-        for (int i = 0; i < kScaleLoads; ++i) {
+        for (int i = 0; i < SL; ++i) {
           if (i < nsl) {
             sreg[i] = buffer_load_u128(rs, 16 * lane, i * 1024);
             if constexpr (AFF) breg[i] = buffer_load_u128(rbs, 16 * lane, i * 1024);
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(1024) void qmv_fast_kernel(
         if constexpr (SLDS) {
           if (jc == 0) {  // this block's scales into the wave's LDS area
 #pragma unroll
-            for (int i = 0; i < kScaleLoads; ++i) {
+            for (int i = 0; i < SL; ++i) {
               if (i < nsl) {
                 if (16 * (lane + 64 * i) < sarea) {
                   *reinterpret_cast<uint4*>(sl + 16 * (lane + 64 * i)) = sreg[i];
@@ -529,22 +531,24 @@ __global__ __launch_bounds__(1024) void qmv_fast_kernel(
             const uint4 w = ring[u][r].w;
             if constexpr (AFF) {
               float D0 = 0.0f, D1 = 0.0f;
-              uint32_t t = w.x & 0x0F0F0F0Fu, q = (w.x >> 4) & 0x0F0F0F0Fu;
+              const uint64_t h01 = (((uint64_t)w.y << 32) | w.x) >> 4;
+              const uint64_t h23 = (((uint64_t)w.w << 32) | w.z) >> 4;
+              uint32_t t = w.x & 0x0F0F0F0Fu, q = (uint32_t)h01 & 0x0F0F0F0Fu;
               D0 = dot2_bf16(x0.x, nibbles_to_bf16x2<false>(t), D0);
               D0 = dot2_bf16(x0.y, nibbles_to_bf16x2<true>(t), D0);
               D0 = dot2_bf16(x0.z, nibbles_to_bf16x2<false>(q), D0);
               D0 = dot2_bf16(x0.w, nibbles_to_bf16x2<true>(q), D0);
-              t = w.y & 0x0F0F0F0Fu, q = (w.y >> 4) & 0x0F0F0F0Fu;
+              t = w.y & 0x0F0F0F0Fu, q = (uint32_t)(h01 >> 32) & 0x0F0F0F0Fu;
               D1 = dot2_bf16(x1.x, nibbles_to_bf16x2<false>(t), D1);
               D1 = dot2_bf16(x1.y, nibbles_to_bf16x2<true>(t), D1);
               D1 = dot2_bf16(x1.z, nibbles_to_bf16x2<false>(q), D1);
               D1 = dot2_bf16(x1.w, nibbles_to_bf16x2<true>(q), D1);
-              t = w.z & 0x0F0F0F0Fu, q = (w.z >> 4) & 0x0F0F0F0Fu;
+              t = w.z & 0x0F0F0F0Fu, q = (uint32_t)h23 & 0x0F0F0F0Fu;
               D0 = dot2_bf16(x2.x, nibbles_to_bf16x2<false>(t), D0);
               D0 = dot2_bf16(x2.y, nibbles_to_bf16x2<true>(t), D0);
               D0 = dot2_bf16(x2.z, nibbles_to_bf16x2<false>(q), D0);
               D0 = dot2_bf16(x2.w, nibbles_to_bf16x2<true>(q), D0);
-              t = w.w & 0x0F0F0F0Fu, q = (w.w >> 4) & 0x0F0F0F0Fu;
+              t = w.w & 0x0F0F0F0Fu, q = (uint32_t)(h23 >> 32) & 0x0F0F0F0Fu;
               D1 = dot2_bf16(x3.x, nibbles_to_bf16x2<false>(t), D1);
               D1 = dot2_bf16(x3.y, nibbles_to_bf16x2<true>(t), D1);
               D1 = dot2_bf16(x3.z, nibbles_to_bf16x2<false>(q), D1);
@@ -631,7 +635,7 @@ hipError_t run(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hip
   const int64_t by_rows = (N + kTeams - 1) / kTeams;
   int64_t grid = (int64_t)device_cu_count() * (lds > 40 * 1024 ? 3 : 4);
   if (nslices > 1 || grid > by_rows) grid = by_rows;
-  hipLaunchKernelGGL((qmv_kernel<MODE, MAXM>), dim3((unsigned)grid), dim3(kThreads), lds, s, x,
+  launch_main(&qmv_kernel<MODE, MAXM>, dim3((unsigned)grid), dim3(kThreads), lds, s, x,
                      M, K, N, reinterpret_cast<const uint4*>(w.codes), w.scales, w.biases,
                      w.global_scale, y, (int)ks, nslices);
   return hipGetLastError();
@@ -670,13 +674,19 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t
   const int K = (int)w.cols;
   const FastShape sh = fast_shape<MODE, R, SLDS>(M, K, NJ, N);
   const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
-  if (sh.lds > 64 * 1024) {  // opt in to the large LDS allocation (160 KB on gfx950)
+  // opt in to the large LDS allocation (160 KB on gfx950), once per device
+  // and size
+  static std::atomic<size_t> lds_granted[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (sh.lds > 64 * 1024 && sh.lds > lds_granted[dev].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
     if (e != hipSuccess) return e;
+    lds_granted[dev].store(sh.lds, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>), dim3((unsigned)sh.grid),
+  launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>, dim3((unsigned)sh.grid),
                      dim3(64 * sh.wpg), sh.lds, s, x, M, K, (int)N, w.codes, w.scales,
                      w.biases, w.global_scale, y, NJ, (int)nblocks);
   return hipGetLastError();
@@ -693,14 +703,14 @@ bool fast_ok(int M, int NJ) {
 }
 
 // Staged scales apply when every row holds whole 32-chunk steps and whole
-// 16-byte scale pieces, the block's scales fit kScaleLoads loads per lane,
+// 16-byte scale pieces, the block's scales fit the scale loads per lane,
 // at most NJ steps are in flight, and the LDS fits.
 template <int MODE, int R>
 bool slds_ok(int K, int NJ, int M, int64_t N) {
   const int cpr = K / 32;
   const int sarea = block_scale_bytes<MODE>(R, K) / (MODE == BSFP_AFFINE ? 2 : 1);
   const int srb = sarea / (2 * R);
-  if (cpr % 32 || srb % 16 || sarea > kScaleLoads * 1024 || kRing / R > NJ) return false;
+  if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || kRing / R > NJ) return false;
   return fast_shape<MODE, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
 }
 
@@ -748,10 +758,10 @@ hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t*
   if (w.cols % 32 != 0) {  // only NVFP4 rows can have K % 32 == 16
     const dim3 grid((unsigned)((w.rows + 3) / 4));
     if (M == 1)
-      hipLaunchKernelGGL(qmv_nvfp4_words_kernel<1>, grid, dim3(kThreads), 0, s, x, M, w.cols,
+      launch_main(&qmv_nvfp4_words_kernel<1>, grid, dim3(kThreads), 0, s, x, M, w.cols,
                          w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, y);
     else
-      hipLaunchKernelGGL(qmv_nvfp4_words_kernel<8>, grid, dim3(kThreads), 0, s, x, M, w.cols,
+      launch_main(&qmv_nvfp4_words_kernel<8>, grid, dim3(kThreads), 0, s, x, M, w.cols,
                          w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, y);
     return hipGetLastError();
   }

@@ -174,6 +174,18 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
                      int32_t act, void* workspace, size_t workspace_bytes,
                      uint16_t* y, bsfp_stream stream);
 
+/*
+ * bsfp_time_next_launch: measurement hook.  The main kernel of this
+ * thread's next bsfp_qmv or bsfp_qmm call (the GEMV, or the GEMM of
+ * bsfp_qmm) is launched with hipExtLaunchKernelGGL, whose start and stop
+ * events then carry that kernel's own begin and end times, with no extra
+ * commands queued between kernels.  start_event and stop_event are hipEvent_t
+ * handles the caller created (timing enabled) and still owns; either may be
+ * NULL.  One-shot: the pair is cleared by the launch that uses it, and
+ * passing two NULLs clears a pending pair.  Always returns BSFP_OK.
+ */
+bsfp_status bsfp_time_next_launch(void* start_event, void* stop_event);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* bsfp_last_error(void);
 

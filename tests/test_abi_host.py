@@ -27,7 +27,8 @@ def blib():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("bsfp_quantize", "bsfp_dequantize", "bsfp_qmv", "bsfp_qmm", "bsfp_amax",
-              "bsfp_qmm_workspace_bytes", "bsfp_last_error", "bsfp_version"):
+              "bsfp_qmm_workspace_bytes", "bsfp_time_next_launch", "bsfp_last_error",
+              "bsfp_version"):
         assert f in fns
 
 
@@ -132,3 +133,11 @@ def test_no_cpu_fallback_in_product(blib):
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, f
+
+
+def test_time_next_launch_set_and_clear(blib):
+    """The measurement hook only stores the pair (no GPU work): OK either way."""
+    L = blib.lib()
+    assert L.bsfp_time_next_launch(None, None) == 0
+    assert L.bsfp_time_next_launch(FAKE, FAKE) == 0
+    assert L.bsfp_time_next_launch(None, None) == 0

@@ -136,3 +136,30 @@ def test_qmv_deterministic(bsfp):
         a = bsfp.qmv(x, q)
         b2 = bsfp.qmv(x, q)
         assert torch.equal(a, b2)
+
+
+def test_launch_event_hook_times_the_gemv(bsfp):
+    """bsfp_time_next_launch: the events bracket the GEMV kernel of the next
+    call only, and the result is the same as without the hook."""
+    import ctypes as C
+    rt = C.CDLL("libamdhip64.so")
+    rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    rt.hipEventDestroy.argtypes = [C.c_void_p]
+    ev = [C.c_void_p(), C.c_void_p()]
+    for e in ev:
+        assert rt.hipEventCreate(C.byref(e)) == 0
+    x = to_dev(S.generic((1, 5120), 1.0, seed=3))
+    q = bsfp.quantize(to_dev(S.generic((8192, 5120), 0.02, seed=4)), 0)
+    ref = bsfp.qmv(x, q)
+    bsfp.time_next_launch(ev[0].value, ev[1].value)
+    y = bsfp.qmv(x, q)
+    y2 = bsfp.qmv(x, q)  # one-shot: this launch is not timed
+    torch.cuda.synchronize()
+    ms = C.c_float()
+    assert rt.hipEventElapsedTime(C.byref(ms), ev[0], ev[1]) == 0
+    assert 0.0 < ms.value < 100.0
+    assert torch.equal(y, ref) and torch.equal(y2, ref)
+    bsfp.time_next_launch(None, None)
+    for e in ev:
+        rt.hipEventDestroy(e)
