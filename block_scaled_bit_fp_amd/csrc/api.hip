@@ -230,6 +230,9 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_
   if (w->cols % 64)
     return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld is not a multiple of 64",
                 (long long)w->cols);
+  if ((reinterpret_cast<uintptr_t>(w->scales) & 3) ||
+      (w->biases && (reinterpret_cast<uintptr_t>(w->biases) & 3)))
+    return fail(BSFP_ERR_ARG, "bsfp_qmm: scales and biases must be 4-byte aligned");
   if (act == BSFP_ACT_SAME && w->mode == BSFP_AFFINE)
     return fail(BSFP_ERR_UNSUPPORTED,
                 "bsfp_qmm: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only");

@@ -1,18 +1,20 @@
 // qmm.hip -- prefill GEMM y[M, N] = x[M, K] . W[N, K]^T on MFMA for gfx950.
 //
-// Two kernels share one tiling scheme (4 waves in a 2 x 2 arrangement, each
-// wave owning WMT x WNT tiles of 32 x 32 outputs, K advanced 64 at a time):
-//
 // gemm_dq_kernel -- 16-bit MFMA (v_mfma_f32_32x32x16_{bf16,f16}) with the
-//   weights dequantized in registers.  The 16-bit A operand (bf16 x, or the
-//   fp16 dequantized NVFP4 activations of the qq path) is staged through LDS
-//   (double-buffered, XOR-swizzled 16-byte chunks so the 32 rows a wave reads
-//   at one k offset fall in different banks).  The packed weight codes never
-//   touch LDS: each lane loads the 16-byte code chunk (32 k-values) of its
-//   own weight row one K-step ahead and expands it right before the MFMA.
-//   The contraction order inside a 64-wide K step is permuted consistently
-//   for both operands: at MFMA step kk, lane half h covers k = 32h + 8kk ..
-//   32h + 8kk + 7, so that each lane reads whole code words.
+//   weights dequantized in registers.  Prefill tiles are 256 x 256 on 8 waves
+//   (each 128 x 64); small M uses narrower M tiles.  Per K step of 64, the
+//   16-bit A tile (bf16 x, or the fp16 dequantized NVFP4 activations of the
+//   qq path), the packed weight codes and their scales all go from global
+//   memory straight into LDS (buffer_load ... lds, issued as inline assembly
+//   so that the compiler adds no conservative waits of its own), three
+//   stages deep: the loads of step s + 2 are in flight while step s runs,
+//   and one explicit vmcnt per step waits for exactly the previous ones.  A
+//   tiles are XOR-swizzled in LDS so ds_read_b128 is conflict-free.  Each
+//   lane reads the 16-byte code chunk (32 k-values) of its weight row from
+//   LDS and expands it right before the MFMA.  The contraction order inside
+//   a 64-wide K step is permuted consistently for both operands: at MFMA
+//   step kk, lane half h covers k = 32h + 8kk .. 32h + 8kk + 7, so that each
+//   lane reads whole code words.
 //     NVFP4 qq (fp16): E2M1 * E4M3 is exact in fp16, so the weight expands
 //       with one v_cvt_scalef32_pk_f16_fp4 and one v_pk_mul_f16 per pair.
 //     NVFP4 weight-only (bf16): E2M1 -> fp32 pair, times the block scale,
@@ -24,7 +26,9 @@
 //       GEMM for nvfp4 prefill"); q comes from the exact fp8-byte decode.
 //   The per-tensor scale (g_w, or alpha = g_x * g_w for qq) is applied in the
 //   epilogue ("mlx 0.30.7.3 -> 0.30.7.6", qqmm_utils.cu: alpha =
-//   amax_x * amax_w / (448*6)^2, read on the device).
+//   amax_x * amax_w / (448*6)^2, read on the device).  When 256 x 256 tiles
+//   would leave a small last round on the CUs, the output columns of that
+//   round go to a second launch with 128 x 64 tiles.
 //
 // gemm_mx_kernel -- MXFP4 x MXFP4 on the CDNA4 block-scaled MFMA
 //   v_mfma_scale_f32_32x32x64_f8f6f4: both operands stay 4-bit, and each
@@ -33,6 +37,8 @@
 //
 // fp32 accumulation, bf16 round-to-nearest-even output, rows and columns
 // beyond M / N clamped on load and masked on store.
+#include <algorithm>
+
 #include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
 
@@ -148,12 +154,41 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// 16 bytes per lane from a buffer straight into LDS: the LDS base is
-// wave-uniform and lane i lands at base + 16 i.  (Kept out of line of the
-// kernel templates: the host pass of hipcc drops a kernel's launch stub when
-// its template body names this builtin directly.)
+// 16 bytes per lane from a buffer straight into LDS: M0 holds the
+// wave-uniform LDS byte offset and lane i lands at M0 + 16 i.  Written as
+// inline assembly on purpose: the compiler does not track it, so it adds no
+// waits of its own before LDS reads of other buffers (it cannot tell the
+// buffers apart and would otherwise hold every read behind every such load);
+// the kernel waits for these loads itself, with an explicit vmcnt before the
+// barrier that publishes the buffer.
 __device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+  typedef __attribute__((address_space(3))) uint4 lds_u4;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u4*)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave still in
+// flight (loads complete in issue order), the direct-to-LDS ones included.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 4 bytes per lane from a buffer straight into LDS (lane i lands at M0 + 4 i),
+// untracked by the compiler like buffer_load_lds16.
+__device__ __forceinline__ void buffer_load_lds4(rsrc_t r, void* lds, int voff, int soff) {
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u32*)lds);
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
+               : "memory");
 }
 
 // Physical 16-byte chunk of logical chunk c in tile row r.  The XOR with r & 7
@@ -185,16 +220,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
     const float* __restrict__ g1, const float* __restrict__ g2, int M, int N, int K,
-    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ Y, int ldy, int tiles_m, int tiles_n) {
   constexpr int NW = WGM * WGN;
   constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
   constexpr int WROWS = BM / NW;  // A rows each wave brings into LDS per K step
   static_assert(WROWS % 8 == 0, "each wave loads whole 8-row LDS blocks");
-  // Two separate LDS arrays (not one array with a computed offset) let the
-  // compiler see that the prefetch into one never aliases reads of the other,
-  // so it does not hold the reads behind the prefetch.
-  __shared__ uint4 lds0[BM * 8];  // [BM][8] 16-byte chunks, swizzled
-  __shared__ uint4 lds1[BM * 8];
+  // Three LDS stages, each [A tile | B codes | B scales | B biases]; K steps
+  // rotate through them and the loads of step s + 2 go out while step s is
+  // computed.  Every global load of the loop goes straight to LDS through
+  // buffer_load_lds16/4, which the compiler does not track: the only wait
+  // for them is the explicit vmcnt before each step's barrier, so two steps
+  // of loads stay in flight.  Every wave issues the same number of loads per
+  // step, which makes that count exact for each wave.
+  constexpr int A_U4 = BM * 8;          // [BM][8] 16-byte chunks, swizzled
+  constexpr int BC_U4 = BN * 2;         // [BN][2] 16-byte code chunks
+  constexpr int BS_U4 = BN / 4;         // [BN] scale dwords
+  constexpr int BB_U4 = (DEC == DEC_AFFINE) ? BN / 4 : 0;  // [BN] bias dwords
+  constexpr int STAGE_U4 = A_U4 + BC_U4 + BS_U4 + BB_U4;
+  __shared__ uint4 smem[3 * STAGE_U4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,9 +248,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   const int m_base = tm * BM, n_base = tn * BN;
   const int rows_m = min(BM, M - m_base), rows_n = min(BN, N - n_base);
 
-  // A: direct buffer -> LDS, 16 bytes per lane per instruction; an instruction
-  // fills 8 consecutive tile rows (lane i -> row i / 8, physical chunk i % 8),
-  // so the swizzle is applied to the source offsets.
+  // A: an instruction fills 8 consecutive tile rows (lane i -> row i / 8,
+  // physical chunk i % 8), so the swizzle is applied to the source offsets.
   const rsrc_t ra = make_rsrc(A + (int64_t)m_base * K, (int64_t)rows_m * K * 2);
   int a_off[WROWS / 8];
 #pragma unroll
@@ -215,29 +257,77 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const int r = wave * WROWS + s * 8 + (lane >> 3);
     a_off[s] = r * K * 2 + swz(r, lane & 7) * 16;
   }
-  auto load_a = [&](int k0, uint4* buf) {
-#pragma unroll
-    for (int s = 0; s < WROWS / 8; ++s) {
-      uint4* dst = buf + (wave * WROWS + s * 8) * 8;
-      buffer_load_lds16(ra, dst, a_off[s], k0 * 2);
-    }
-  };
 
-  // B: the lane's weight rows within the tile
+  // B codes: 16-byte piece p of the tile's step is row p / 2, half p % 2;
+  // each wave loads PPW consecutive pieces.
+  constexpr int PPW = 2 * BN / NW;
+  constexpr int BC_LOADS = (PPW + 63) / 64;
+  static_assert(PPW * NW == 2 * BN && (PPW >= 64 ? PPW % 64 == 0 : 64 % PPW == 0),
+                "code pieces split evenly over the waves");
   const rsrc_t rc = make_rsrc(codes + (int64_t)n_base * (K / 8), (int64_t)rows_n * (K / 2));
+  // B scales (and affine biases): one dword per tile row and step, read by
+  // BN / NW lanes of each wave.  NVFP4 needs 4 bytes per row and step (four
+  // E4M3 blocks of 16); MXFP4 and affine need 2, taken from the aligned dword
+  // that holds them.
   constexpr int gsz = (DEC == DEC_AFFINE) ? 64 : (DEC == DEC_MXFP4) ? 32 : 16;
   constexpr int sbytes = (DEC == DEC_AFFINE) ? 2 : 1;
-  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) +
-                                  (int64_t)n_base * (K / gsz) * sbytes,
-                              (int64_t)rows_n * (K / gsz) * sbytes);
+  constexpr int SROWS = BN / NW;  // scale rows per wave
+  static_assert(SROWS <= 64, "one scale load per wave and array");
+  const int srb = (K / gsz) * sbytes;  // scale bytes per weight row
+  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * srb,
+                              (int64_t)rows_n * srb);
   const rsrc_t rb = make_rsrc(biases ? biases + (int64_t)n_base * (K / 64) : nullptr,
-                              biases ? (int64_t)rows_n * (K / 64) * 2 : 0);
+                              biases ? (int64_t)rows_n * srb : 0);
+  const int srow = wave * SROWS + lane;  // the tile row whose scales this lane loads
+
+  auto stage = [&](int i) { return smem + i * STAGE_U4; };
+  auto load_step = [&](int st, uint4* sb) {
+    const int k0 = st * 64;
+#pragma unroll
+    for (int s = 0; s < WROWS / 8; ++s)
+      buffer_load_lds16(ra, sb + (wave * WROWS + s * 8) * 8, a_off[s], k0 * 2);
+    uint4* bc = sb + A_U4;
+#pragma unroll
+    for (int c = 0; c < BC_LOADS; ++c) {
+      const int p0 = wave * PPW + c * 64;
+      const int p = p0 + lane;
+      if (PPW >= 64 || lane < PPW)
+        buffer_load_lds16(rc, bc + p0, (p >> 1) * (K / 2) + (p & 1) * 16, k0 / 2);
+    }
+    if (lane < SROWS) {
+      const int so = (DEC == DEC_NVFP4 || DEC == DEC_NVFP4_F16) ? srow * srb + 4 * st
+                                                                 : (srow * srb + 2 * st) & ~3;
+      buffer_load_lds4(rs, sb + A_U4 + BC_U4 + wave * SROWS / 4, so, 0);
+      if constexpr (DEC == DEC_AFFINE)
+        buffer_load_lds4(rb, sb + A_U4 + BC_U4 + BS_U4 + wave * SROWS / 4, so, 0);
+    }
+  };
+  // vector-memory loads one step issues per wave
+  constexpr int kStepLoads = WROWS / 8 + BC_LOADS + ((DEC == DEC_AFFINE) ? 2 : 1);
+
+  // this lane's weight rows within the tile
   int nl[WNT];
 #pragma unroll
   for (int j = 0; j < WNT; ++j) nl[j] = wn * 32 * WNT + 32 * j + l32;
-  auto load_b = [&](int k0, BFrag (&dst)[WNT]) {
+  auto read_b = [&](const uint4* sb, int st, BFrag (&dst)[WNT]) {
+    const uint4* bc = sb + A_U4;
+    const uint8_t* bs = reinterpret_cast<const uint8_t*>(sb + A_U4 + BC_U4);
 #pragma unroll
-    for (int j = 0; j < WNT; ++j) load_bfrag_buf<DEC>(dst[j], rc, rs, rb, nl[j], K, k0, h);
+    for (int j = 0; j < WNT; ++j) {
+      dst[j].codes = bc[nl[j] * 2 + h];
+      if constexpr (DEC == DEC_NVFP4 || DEC == DEC_NVFP4_F16) {
+        // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
+        dst[j].s0 = *reinterpret_cast<const uint16_t*>(bs + nl[j] * 4 + 2 * h);
+      } else {
+        const int hw = ((nl[j] + n_base) * srb + 2 * st) & 2;  // byte offset in the dword
+        if constexpr (DEC == DEC_MXFP4) {
+          dst[j].s0 = bs[nl[j] * 4 + hw + h];
+        } else {
+          dst[j].s0 = *reinterpret_cast<const uint16_t*>(bs + nl[j] * 4 + hw);
+          dst[j].s1 = *reinterpret_cast<const uint16_t*>(bs + BS_U4 * 16 + nl[j] * 4 + hw);
+        }
+      }
+    }
   };
 
   f32x16_t acc[WMT][WNT];
@@ -248,40 +338,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // One K step: wait until every wave's loads for this step have landed,
-  // issue the next step's loads into the other buffer, then run the MFMAs.
-  auto step = [&](int k0, uint4* cur_lds, uint4* nxt_lds, BFrag (&cur)[WNT],
-                  BFrag (&nxt)[WNT]) {
-    wait_vmem();
+  // One K step: wait for this step's loads (those of the next step stay in
+  // flight), make every wave's loads visible, issue the loads of the step
+  // after next into the stage the previous step used, then run the MFMAs.
+  // Past the last step the loads repeat the last step into a stage nobody
+  // reads, so every step has the same loads in flight.
+  const int nsteps = K / 64;
+  auto step = [&](int st, int si, int pi) {
+    wait_vmem_le<kStepLoads>();
     __syncthreads();
-    if (k0 + 64 < K) {
-      load_a(k0 + 64, nxt_lds);
-      load_b(k0 + 64, nxt);
-    }
+    load_step(min(st + 2, nsteps - 1), stage(pi));
+    const uint4* cur = stage(si);
+    BFrag b[WNT];
+    read_b(cur, st, b);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 a[WMT];
 #pragma unroll
       for (int i = 0; i < WMT; ++i) {
         const int r = wm * 32 * WMT + 32 * i + l32;
-        a[i] = cur_lds[r * 8 + swz(r, 4 * h + kk)];
+        a[i] = cur[r * 8 + swz(r, 4 * h + kk)];
       }
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        const Op8 b = expand<DEC>(cur[j], kk);
+        const Op8 bo = expand<DEC>(b[j], kk);
 #pragma unroll
-        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], b, acc[i][j]);
+        for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], bo, acc[i][j]);
       }
     }
   };
 
-  BFrag b0[WNT], b1[WNT];
-  load_a(0, lds0);
-  load_b(0, b0);
-  for (int k0 = 0; k0 < K; k0 += 128) {
-    step(k0, lds0, lds1, b0, b1);
-    if (k0 + 64 < K) step(k0 + 64, lds1, lds0, b1, b0);
+  load_step(0, stage(0));
+  load_step(min(1, nsteps - 1), stage(1));
+  int st = 0;
+  for (; st + 3 <= nsteps; st += 3) {
+    step(st, 0, 2);
+    step(st + 1, 1, 0);
+    step(st + 2, 2, 1);
   }
+  if (st < nsteps) step(st, 0, 2);
+  if (st + 1 < nsteps) step(st + 1, 1, 0);
+  wait_vmem();  // the surplus loads land before the LDS is released
 
   const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
   const bool full = (rows_m == BM) && (rows_n == BN);
@@ -291,17 +388,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     for (int j = 0; j < WNT; ++j) {
       const int n = n_base + wn * 32 * WNT + 32 * j + l32;
       const int m0 = m_base + wm * 32 * WMT + 32 * i + 4 * h;
-      uint16_t* yp = Y + (int64_t)m0 * N + n;
+      uint16_t* yp = Y + (int64_t)m0 * ldy + n;
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+          yp[(int64_t)(8 * (r >> 2) + (r & 3)) * ldy] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 8 * (r >> 2) + (r & 3);
           if (m < M && n < N)
-            yp[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+            yp[(int64_t)(8 * (r >> 2) + (r & 3)) * ldy] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
         }
       }
     }
@@ -386,16 +483,62 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     }
 }
 
+// Launch of gemm_dq_kernel on the output columns [n0, n0 + n) of y (weight
+// rows n0 .. n0 + n - 1), with the given launch events.
+template <int DEC, int WGM, int WGN, int WMT, int WNT>
+void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int n,
+               const float* g1, const float* g2, uint16_t* y, hipStream_t s, hipEvent_t ev0,
+               hipEvent_t ev1) {
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int gsz = (DEC == DEC_AFFINE) ? 64 : (DEC == DEC_MXFP4) ? 32 : 16;
+  const int sbytes = (DEC == DEC_AFFINE) ? 2 : 1;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (n + BN - 1) / BN;
+  const uint32_t* codes = w.codes + n0 * (K / 8);
+  const void* scales = reinterpret_cast<const uint8_t*>(w.scales) + n0 * (K / gsz) * sbytes;
+  const uint16_t* biases = w.biases ? w.biases + n0 * (K / 64) : nullptr;
+  auto kern = &gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>;
+  const dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kern, grid, block, 0u, s, ev0, ev1, 0u, A, codes, scales, biases, g1,
+                          g2, M, n, K, y + n0, N, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL(kern, grid, block, 0, s, A, codes, scales, biases, g1, g2, M, n, K,
+                       y + n0, N, tiles_m, tiles_n);
+}
+
 template <int DEC, int WGM, int WGN, int WMT, int WNT>
 hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
                   const float* g2, uint16_t* y, hipStream_t s) {
-  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
-  const int N = (int)w.rows, K = (int)w.cols;
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  launch_main(&gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>, dim3(tiles_m * tiles_n),
-                     dim3(64 * WGM * WGN), 0, s, A, w.codes, w.scales, w.biases, g1, g2, M, N,
-                     K, y, tiles_m, tiles_n);
+  const LaunchEvents ev = take_launch_events();
+  launch_dq<DEC, WGM, WGN, WMT, WNT>(A, M, w, 0, (int)w.rows, g1, g2, y, s, ev.start, ev.stop);
+  return hipGetLastError();
+}
+
+// Big tiles (256 x 256, 8 waves) for prefill row counts.  When the tiles
+// fill the CUs for some whole rounds plus a small last round (800 tiles on
+// 256 CUs: 3 rounds and an eighth), most CUs would idle through that last
+// round; instead the weight rows of the whole rounds run with big tiles and
+// the remaining rows in a second launch of 128 x 64 tiles, which spreads
+// them over all CUs.
+template <int DEC>
+hipError_t run_dq_big(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
+                      const float* g2, uint16_t* y, hipStream_t s) {
+  const int N = (int)w.rows;
+  const int cus = device_cu_count();
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int64_t rounds = tiles / cus;
+  const int64_t rest = tiles - rounds * cus;
+  const int n_main = (int)std::min<int64_t>(tiles_n, rounds * cus / tiles_m) * 256;
+  const LaunchEvents ev = take_launch_events();
+  if (rounds == 0 || rest * 2 > cus || n_main <= 0 || n_main >= N) {
+    launch_dq<DEC, 2, 4, 4, 2>(A, M, w, 0, N, g1, g2, y, s, ev.start, ev.stop);
+    return hipGetLastError();
+  }
+  launch_dq<DEC, 2, 4, 4, 2>(A, M, w, 0, n_main, g1, g2, y, s, ev.start, nullptr);
+  launch_dq<DEC, 2, 2, 2, 1>(A, M, w, n_main, N - n_main, g1, g2, y, s, nullptr, ev.stop);
   return hipGetLastError();
 }
 
@@ -406,7 +549,7 @@ hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float
                     const float* g2, uint16_t* y, hipStream_t s) {
   if (M <= 64) return run_dq<DEC, 1, 4, 2, 2>(A, M, w, g1, g2, y, s);
   if (M <= 128) return run_dq<DEC, 2, 4, 2, 2>(A, M, w, g1, g2, y, s);
-  return run_dq<DEC, 2, 4, 4, 2>(A, M, w, g1, g2, y, s);
+  return run_dq_big<DEC>(A, M, w, g1, g2, y, s);
 }
 
 hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,

@@ -109,16 +109,19 @@ def _sampled_qq(o, b, M, N, K, seed, n_rows=8, n_pairs=2048, x=None, w=None):
     return e
 
 
-@pytest.mark.parametrize("M", [1134, 2048])
+@pytest.mark.parametrize("M", [1134, 2048, 4096])
 def test_nvfp4_prefill_qq_sampled_full_size(oracle_mod, bsfp, M):
     """X[M,5120] x W[25600,5120]^T at full size: 8 full output rows plus
-    2048 random outputs computed one by one by the oracle."""
+    2048 random outputs computed one by one by the oracle.  At M = 2048 and
+    4096 the last 1024 output columns come from the second (small-tile)
+    launch; the full rows cover them."""
     e = _sampled_qq(oracle_mod, bsfp, M, 25600, 5120, seed=5)
     assert e.max() <= QQ_TOL, e.max()
 
 
 def test_affine_weight_only_extra_shape_sampled(oracle_mod, bsfp):
-    """x[2048,5120] . W_up[25600,5120]^T, affine weight-only, sampled."""
+    """x[2048,5120] . W_up[25600,5120]^T, affine weight-only, sampled (the
+    sample spans both the big-tile and the small-tile column ranges)."""
     o = oracle_mod
     x = S.generic((2048, 5120), 1.0, seed=6)
     _, w = S.affine_decode("up")
