@@ -351,21 +351,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint4* cur = stage(si);
     BFrag b[WNT];
     read_b(cur, st, b);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 a[WMT];
+    // A fragments of sub-step kk + 1 are read while kk's MFMAs run
+    auto read_a = [&](int kk, uint4 (&a)[WMT]) {
 #pragma unroll
       for (int i = 0; i < WMT; ++i) {
         const int r = wm * 32 * WMT + 32 * i + l32;
         a[i] = cur[r * 8 + swz(r, 4 * h + kk)];
       }
+    };
+    auto mma = [&](int kk, const uint4 (&a)[WMT]) {
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const Op8 bo = expand<DEC>(b[j], kk);
 #pragma unroll
         for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], bo, acc[i][j]);
       }
-    }
+    };
+    uint4 a0[WMT], a1[WMT];
+    read_a(0, a0);
+    read_a(1, a1);
+    mma(0, a0);
+    read_a(2, a0);
+    mma(1, a1);
+    read_a(3, a1);
+    mma(2, a0);
+    mma(3, a1);
   };
 
   load_step(0, stage(0));
