@@ -15,7 +15,9 @@ already resident in HBM:
   qqmm        NVFP4 prefill X[2048,5120] . W[25600,5120]^T (x quantized on the
               fly, alpha = g_x g_w), the headline GEMM
   qqmm_1134 / qqmm_4096   the same GEMM at M = 1134 and 4096
-  qmm_mx      MXFP4 qq GEMM on the scaled MFMA, M = 32 and 512
+  qq_decode   NVFP4 qq product at M = 1 on W[25600,5120] (x quantized and
+              dequantized exactly, then the GEMV; alpha = g_x g_w)
+  qmm_mx32 / qmm_mx512   MXFP4 qq GEMM on the scaled MFMA, W[5760,2880]
   qmm_affine  affine weight-only x[2048,5120] . W_up[25600,5120]^T
 
 The JSON line reports the headline metric: `value` is the sustained qmv GB/s
@@ -174,16 +176,22 @@ def main():
     def qq(M):
         return lambda: b.qmm(X_pf[M], q_pf, act="same", workspace=ws_pf[M], out=Y_pf[M])
 
-    def st_qmm_mx():
-        for M in (32, 512):
-            b.qmm(x_mx[M], q_mx, act="same", workspace=ws_mx[M], out=y_mx[M])
+    ws_dec = torch.empty(b.qmm_workspace_bytes(b.NVFP4, 1, HIDDEN, "same"), dtype=torch.uint8,
+                         device=dev)
+
+    def st_qq_decode():
+        b.qmm(x_nv1, q_pf, act="same", workspace=ws_dec, out=y_nv1)
+
+    def mx(M):
+        return lambda: b.qmm(x_mx[M], q_mx, act="same", workspace=ws_mx[M], out=y_mx[M])
 
     def st_qmm_affine():
         b.qmm(X_aff, q_up0, act="bf16", out=Y_aff)
 
     stages = [("act_quant", st_act_quant), ("dequant", st_dequant), ("w_quant", st_w_quant),
               ("qmv_sweep", st_qmv_sweep), ("qmv_fp4", st_qmv_fp4), ("qqmm", qq(2048)),
-              ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qmm_mx", st_qmm_mx),
+              ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qq_decode", st_qq_decode),
+              ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)),
               ("qmm_affine", st_qmm_affine)]
     if args.only:
         keep = set(args.only.split(","))
@@ -277,8 +285,15 @@ def main():
                 out[f"qmm_tflops_m{M}"] = round(2.0 * M * INTER * HIDDEN / (ms[key] * 1e-3) / 1e12, 1)
     if "qmm_affine" in ms:
         out["qmm_affine_tflops"] = round(2.0 * 2048 * INTER * HIDDEN / (ms["qmm_affine"] * 1e-3) / 1e12, 1)
-    if "qmm_mx" in ms:
-        out["qmm_mx_ms"] = stage_ms["qmm_mx"]
+    if "qq_decode" in ms:
+        out["qq_decode_gbs"] = round(fp4_bytes(INTER, HIDDEN, 16) / (ms["qq_decode"] * 1e-3) / 1e9, 1)
+    if "qmm_mx32" in ms:  # HBM-bound size: weight + activation bytes per call
+        out["qmm_mx32_gbs"] = round((fp4_bytes(5760, 2880, 32, 32) + 32 * 2880 * 2)
+                                    / (ms["qmm_mx32"] * 1e-3) / 1e9, 1)
+    if "qmm_mx512" in ms:  # against the dense FP4 MFMA peak
+        tf = 2.0 * 512 * 5760 * 2880 / (ms["qmm_mx512"] * 1e-3) / 1e12
+        out["qmm_mx512_tflops"] = round(tf, 1)
+        out["qmm_mx512_frac_fp4"] = round(tf / FP4_PEAK_TFS, 4)
     if "act_quant" in ms:
         nbytes = 4096 * HIDDEN * 2 * 2 + 4096 * HIDDEN // 2 + 4096 * HIDDEN // 16
         out["act_quant_gbs"] = round(nbytes / (ms["act_quant"] * 1e-3) / 1e9, 1)

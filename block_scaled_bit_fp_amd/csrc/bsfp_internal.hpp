@@ -47,6 +47,13 @@ hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* c
 hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words, void* xhat,
                                              const float* g_src, int g_src_is_amax,
                                              float* g_out, hipStream_t s);
+// As above with bf16 output (the x of the qq decode GEMV).
+hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
+                                              const float* g_src, int g_src_is_amax,
+                                              float* g_out, hipStream_t s);
+// MXFP4 quantize, then exact dequantization to bf16.
+hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
+                                              hipStream_t s);
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, hipStream_t s);
 hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* codes,
@@ -55,8 +62,10 @@ hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* 
 hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s);
 
 // ---- qmv (qmv.hip)
+// g2: optional second device scale multiplied into the output (the qq decode
+// path passes g_x there).
 hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
-                      hipStream_t s);
+                      hipStream_t s, const float* g2 = nullptr);
 
 // ---- qmm (qmm.hip)
 size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act);

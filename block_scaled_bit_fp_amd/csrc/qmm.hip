@@ -580,10 +580,17 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace for the qq paths:
 //   NVFP4: [amax f32, g_x f32] (256 B) + xhat fp16 [M, K]
 //   MXFP4: x codes uint32 [M, K/8] + x scales uint8 [M, K/32]
+// Rows of x up to which the qq product runs as a GEMV on the exactly
+// dequantized x (the decode path) instead of a GEMM.
+constexpr int64_t kQqDecodeRows = 8;
+
 size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act) {
   if (act != BSFP_ACT_SAME) return 0;
   if (mode == BSFP_NVFP4) return 256 + align256((size_t)M * K * 2);
-  if (mode == BSFP_MXFP4) return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+  if (mode == BSFP_MXFP4) {
+    if (M <= kQqDecodeRows) return align256((size_t)M * K * 2);
+    return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+  }
   return 0;
 }
 
@@ -598,6 +605,31 @@ hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int
     }
   }
   const int64_t n = M64 * w.cols;
+  if (M64 <= kQqDecodeRows) {
+    // qq decode: x is quantized with w's mode and dequantized exactly to bf16
+    // (E2M1 * E4M3 and E2M1 * 2^e fit bf16), then the GEMV runs on it with
+    // the output scaled by alpha = g_x * g_w (NVFP4 with a global scale on w)
+    // -- the same product as the GEMM path, at every M.
+    if (w.mode == BSFP_NVFP4) {
+      float* amax = reinterpret_cast<float*>(ws);
+      float* gx = amax + 1;
+      uint16_t* xhat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + 256);
+      hipError_t e = hipSuccess;
+      if (w.global_scale) {
+        e = launch_amax(x, n, amax, s);
+        if (e == hipSuccess) e = launch_quantize_dequant_nvfp4_bf16(x, n / 8, xhat, amax, 1, gx, s);
+        if (e != hipSuccess) return e;
+        return launch_qmv(xhat, M, w, y, s, gx);
+      }
+      e = launch_quantize_dequant_nvfp4_bf16(x, n / 8, xhat, nullptr, 0, nullptr, s);
+      if (e != hipSuccess) return e;
+      return launch_qmv(xhat, M, w, y, s);
+    }
+    uint16_t* xhat = reinterpret_cast<uint16_t*>(ws);
+    const hipError_t e = launch_quantize_dequant_mxfp4_bf16(x, n / 8, xhat, s);
+    if (e != hipSuccess) return e;
+    return launch_qmv(xhat, M, w, y, s);
+  }
   if (w.mode == BSFP_NVFP4) {
     float* amax = reinterpret_cast<float*>(ws);
     float* gx = amax + 1;

@@ -89,7 +89,7 @@ template <int MODE, int MAXM>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t N,
     const uint4* __restrict__ codes, const void* __restrict__ scales,
-    const uint16_t* __restrict__ biases, const float* __restrict__ gptr,
+    const uint16_t* __restrict__ biases, const float* __restrict__ gptr, const float* __restrict__ g2ptr,
     uint16_t* __restrict__ y, int ks, int nslices) {
   extern __shared__ uint4 smem[];
   constexpr bool AFF = (MODE == BSFP_AFFINE);
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
   const int lt = threadIdx.x % kTeam;
   const int64_t cpr = K / 32;                 // chunks per row
   const int ipr = (nch + kTeam - 1) / kTeam;  // items per lane per row and slice
-  const float g = (MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f;
+  const float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
 
   // rows of this team: gt, gt + T, gt + 2T, ... (T = teams in the grid)
   const int64_t gt = (int64_t)blockIdx.x * kTeams + team;
@@ -238,11 +238,11 @@ template <int MAXM>
 __global__ __launch_bounds__(kThreads) void qmv_nvfp4_words_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t N,
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ gptr, uint16_t* __restrict__ y) {
+    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= N) return;
-  const float g = gptr ? *gptr : 1.0f;
+  const float g = (gptr ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
   const int64_t wpr = K / 8;
   float acc[MAXM];
 #pragma unroll
@@ -374,7 +374,7 @@ template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
 __global__ __launch_bounds__(1024) void qmv_fast_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const float* __restrict__ gptr, uint16_t* __restrict__ y, int NJ, int nblocks) {
+    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y, int NJ, int nblocks) {
   static_assert(!(SLDS && RAGGED), "staged scales need whole 32-chunk steps");
   constexpr bool AFF = (MODE == BSFP_AFFINE);
   constexpr int PJ = kRing / R;  // steps in flight
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(1024) void qmv_fast_kernel(
   const int nb_wg = nblocks > wg ? (nblocks - wg + G - 1) / G : 0;
   const int passes = wave_in_wg < nb_wg ? (nb_wg - wave_in_wg + wpg - 1) / wpg : 0;
   const int steps = passes * NJ;
-  const float g = (MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f;
+  const float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
 
   // this wave's scale area (SLDS): [2R rows][srb] scales, then the biases
   const int sarea = 2 * R * srb;
@@ -620,7 +620,8 @@ size_t lds_bytes(int64_t k) {
 }
 
 template <int MODE, int MAXM>
-hipError_t run(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hipStream_t s) {
+hipError_t run(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2, uint16_t* y,
+               hipStream_t s) {
   const int64_t N = w.rows, K = w.cols;
   constexpr int64_t gran = (MODE == BSFP_AFFINE) ? 64 : 32;  // whole groups per slice
   int64_t ks = K;
@@ -637,7 +638,7 @@ hipError_t run(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hip
   if (nslices > 1 || grid > by_rows) grid = by_rows;
   launch_main(&qmv_kernel<MODE, MAXM>, dim3((unsigned)grid), dim3(kThreads), lds, s, x,
                      M, K, N, reinterpret_cast<const uint4*>(w.codes), w.scales, w.biases,
-                     w.global_scale, y, (int)ks, nslices);
+                     w.global_scale, g2, y, (int)ks, nslices);
   return hipGetLastError();
 }
 
@@ -668,8 +669,8 @@ FastShape fast_shape(int M, int K, int NJ, int64_t N) {
 }
 
 template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
-hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, int NJ,
-                       hipStream_t s) {
+hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
+                       uint16_t* y, int NJ, hipStream_t s) {
   const int64_t N = w.rows;
   const int K = (int)w.cols;
   const FastShape sh = fast_shape<MODE, R, SLDS>(M, K, NJ, N);
@@ -688,7 +689,7 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t
   }
   launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>, dim3((unsigned)sh.grid),
                      dim3(64 * sh.wpg), sh.lds, s, x, M, K, (int)N, w.codes, w.scales,
-                     w.biases, w.global_scale, y, NJ, (int)nblocks);
+                     w.biases, w.global_scale, g2, y, NJ, (int)nblocks);
   return hipGetLastError();
 }
 
@@ -715,7 +716,8 @@ bool slds_ok(int K, int NJ, int M, int64_t N) {
 }
 
 template <int MODE>
-hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hipStream_t s) {
+hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2, uint16_t* y,
+                hipStream_t s) {
   const int K = (int)w.cols;
   const int NJ = (int)((w.cols / 32 + 31) / 32);
   const bool ragged = (w.cols / 32) % 32 != 0;
@@ -725,50 +727,50 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y, hi
       const int64_t want = 8LL * device_cu_count();
       const int64_t N = w.rows;
       if (N >= 8 * want && slds_ok<MODE, 4>(K, NJ, M, N))
-        return launch_fast<MODE, 1, 4, false, true>(x, M, w, y, NJ, s);
+        return launch_fast<MODE, 1, 4, false, true>(x, M, w, g2, y, NJ, s);
       if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, M, N))
-        return launch_fast<MODE, 1, 2, false, true>(x, M, w, y, NJ, s);
-      if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true>(x, M, w, y, NJ, s);
-      if (slds_ok<MODE, 2>(K, NJ, M, N)) return launch_fast<MODE, 1, 2, false, true>(x, M, w, y, NJ, s);
-      if (slds_ok<MODE, 4>(K, NJ, M, N)) return launch_fast<MODE, 1, 4, false, true>(x, M, w, y, NJ, s);
-      if (ragged) return launch_fast<MODE, 1, 1, true, false>(x, M, w, y, NJ, s);
-      return launch_fast<MODE, 1, 1, false, false>(x, M, w, y, NJ, s);
+        return launch_fast<MODE, 1, 2, false, true>(x, M, w, g2, y, NJ, s);
+      if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true>(x, M, w, g2, y, NJ, s);
+      if (slds_ok<MODE, 2>(K, NJ, M, N)) return launch_fast<MODE, 1, 2, false, true>(x, M, w, g2, y, NJ, s);
+      if (slds_ok<MODE, 4>(K, NJ, M, N)) return launch_fast<MODE, 1, 4, false, true>(x, M, w, g2, y, NJ, s);
+      if (ragged) return launch_fast<MODE, 1, 1, true, false>(x, M, w, g2, y, NJ, s);
+      return launch_fast<MODE, 1, 1, false, false>(x, M, w, g2, y, NJ, s);
     }
     if (ragged) {
-      if (M == 2) return launch_fast<MODE, 2, 1, true, false>(x, M, w, y, NJ, s);
-      if (M <= 4) return launch_fast<MODE, 4, 1, true, false>(x, M, w, y, NJ, s);
-      return launch_fast<MODE, 8, 1, true, false>(x, M, w, y, NJ, s);
+      if (M == 2) return launch_fast<MODE, 2, 1, true, false>(x, M, w, g2, y, NJ, s);
+      if (M <= 4) return launch_fast<MODE, 4, 1, true, false>(x, M, w, g2, y, NJ, s);
+      return launch_fast<MODE, 8, 1, true, false>(x, M, w, g2, y, NJ, s);
     }
-    if (M == 2) return launch_fast<MODE, 2, 1, false, false>(x, M, w, y, NJ, s);
-    if (M <= 4) return launch_fast<MODE, 4, 1, false, false>(x, M, w, y, NJ, s);
-    return launch_fast<MODE, 8, 1, false, false>(x, M, w, y, NJ, s);
+    if (M == 2) return launch_fast<MODE, 2, 1, false, false>(x, M, w, g2, y, NJ, s);
+    if (M <= 4) return launch_fast<MODE, 4, 1, false, false>(x, M, w, g2, y, NJ, s);
+    return launch_fast<MODE, 8, 1, false, false>(x, M, w, g2, y, NJ, s);
   }
   // x too large for one LDS copy: walk K in slices
-  if (M == 1) return run<MODE, 1>(x, M, w, y, s);
-  if (M == 2) return run<MODE, 2>(x, M, w, y, s);
-  if (M <= 4) return run<MODE, 4>(x, M, w, y, s);
-  return run<MODE, 8>(x, M, w, y, s);
+  if (M == 1) return run<MODE, 1>(x, M, w, g2, y, s);
+  if (M == 2) return run<MODE, 2>(x, M, w, g2, y, s);
+  if (M <= 4) return run<MODE, 4>(x, M, w, g2, y, s);
+  return run<MODE, 8>(x, M, w, g2, y, s);
 }
 
 }  // namespace
 
 hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
-                      hipStream_t s) {
+                      hipStream_t s, const float* g2) {
   if (w.rows == 0) return hipGetLastError();
   if (w.cols % 32 != 0) {  // only NVFP4 rows can have K % 32 == 16
     const dim3 grid((unsigned)((w.rows + 3) / 4));
     if (M == 1)
       launch_main(&qmv_nvfp4_words_kernel<1>, grid, dim3(kThreads), 0, s, x, M, w.cols,
-                         w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, y);
+                         w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, g2, y);
     else
       launch_main(&qmv_nvfp4_words_kernel<8>, grid, dim3(kThreads), 0, s, x, M, w.cols,
-                         w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, y);
+                         w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, g2, y);
     return hipGetLastError();
   }
   switch (w.mode) {
-    case BSFP_AFFINE: return by_m<BSFP_AFFINE>(x, M, w, y, s);
-    case BSFP_MXFP4: return by_m<BSFP_MXFP4>(x, M, w, y, s);
-    default: return by_m<BSFP_NVFP4>(x, M, w, y, s);
+    case BSFP_AFFINE: return by_m<BSFP_AFFINE>(x, M, w, g2, y, s);
+    case BSFP_MXFP4: return by_m<BSFP_MXFP4>(x, M, w, g2, y, s);
+    default: return by_m<BSFP_NVFP4>(x, M, w, g2, y, s);
   }
 }
 

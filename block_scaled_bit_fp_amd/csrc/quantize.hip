@@ -31,6 +31,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Byte SEL of w (two E2M1 codes) times the fp32 scale s, as a bf16 pair.
+// The products are exact in fp32 and, for E4M3 or power-of-two scales, in
+// bf16 as well, so the rounding in the pack never changes a value.
+template <int SEL>
+__device__ __forceinline__ uint32_t dq_pair_bf16(uint32_t w, float s) {
+  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return pack_bf16x2(v.x * s, v.y * s);
+}
+
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
   f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
@@ -132,7 +141,10 @@ __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
 // operand of the NVFP4 qq GEMM (the pages' fp_quantize_dequantize, "mlx
 // 0.30.7.3 -> 0.30.7.6", qqmm.cpp); the codes and scales are those
 // bsfp_quantize produces for the same input and global scale.
-__global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_f16_kernel(
+//   BF16 = true writes bf16 instead (E2M1 * E4M3 has at most 6 significant
+//   bits, so it is exact in bf16 too): the x of the qq decode GEMV.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint4* __restrict__ xhat,
     const float* __restrict__ g_src, int g_src_is_amax, float* __restrict__ g_out) {
   float g = 1.0f;
@@ -160,12 +172,20 @@ __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_f16_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
       const uint32_t w = e2m1_pack8(v);
-      const _Float16 sh = (_Float16)e4m3_decode(S);  // exact in fp16
-      const f16x2_t s2 = {sh, sh};
-      o.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
-      o.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
-      o.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
-      o.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
+      if constexpr (BF16) {
+        const float sf = e4m3_decode(S);
+        o.x = dq_pair_bf16<0>(w, sf);
+        o.y = dq_pair_bf16<1>(w, sf);
+        o.z = dq_pair_bf16<2>(w, sf);
+        o.w = dq_pair_bf16<3>(w, sf);
+      } else {
+        const _Float16 sh = (_Float16)e4m3_decode(S);  // exact in fp16
+        const f16x2_t s2 = {sh, sh};
+        o.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
+        o.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
+        o.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
+        o.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
+      }
     }
     xhat[i] = o;
   }
@@ -194,6 +214,37 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
     for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
     codes[i] = e2m1_pack8(v);
     if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+  }
+}
+
+// MXFP4 quantize followed by exact dequantization, written as bf16: the x of
+// the qq decode GEMV (E2M1 * 2^e is exact in bf16 for the exponents a bf16
+// input can produce).  Codes and exponents are those quantize_mxfp4_kernel
+// produces.
+__global__ __launch_bounds__(kThreads) void quantize_dequant_mxfp4_bf16_kernel(
+    const uint4* __restrict__ x, int64_t n_words, uint4* __restrict__ xhat) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = team_max<4>(a);
+    const int be = (int)(__float_as_uint(a) >> 23);
+    const int e = max(be - 129, -127);
+    const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
+    const uint32_t w = e2m1_pack8(v);
+    const float sc = ldexpf(1.0f, e);  // 2^e, subnormal for e = -127
+    uint4 o;
+    o.x = dq_pair_bf16<0>(w, sc);
+    o.y = dq_pair_bf16<1>(w, sc);
+    o.z = dq_pair_bf16<2>(w, sc);
+    o.w = dq_pair_bf16<3>(w, sc);
+    xhat[i] = o;
   }
 }
 
@@ -307,9 +358,26 @@ hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* c
 hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words, void* xhat,
                                              const float* g_src, int g_src_is_amax,
                                              float* g_out, hipStream_t s) {
-  hipLaunchKernelGGL(quantize_dequant_nvfp4_f16_kernel, dim3(stream_grid(n_words)),
+  hipLaunchKernelGGL(quantize_dequant_nvfp4_kernel<false>, dim3(stream_grid(n_words)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
                      reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
+                                              const float* g_src, int g_src_is_amax,
+                                              float* g_out, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_dequant_nvfp4_kernel<true>, dim3(stream_grid(n_words)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
+                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
+                                              hipStream_t s) {
+  hipLaunchKernelGGL(quantize_dequant_mxfp4_bf16_kernel, dim3(stream_grid(n_words)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
+                     reinterpret_cast<uint4*>(xhat));
   return hipGetLastError();
 }
 

@@ -162,7 +162,10 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
  *     computed here), else 1.  The pages' alpha = amax_x*amax_w/(448*6)^2
  *     (create_nvfp4_scalars) is the same quantity up to fp32 rounding.
  *     MXFP4 runs on the gfx950 scaled f8f6f4 MFMA; NVFP4 and AFFINE on bf16
- *     MFMA with both operands dequantized exactly.
+ *     MFMA with both operands dequantized exactly.  For M <= 8 (decode) the
+ *     same product runs as the GEMV of bsfp_qmv on q(x) dequantized exactly
+ *     to bf16, with alpha applied the same way (the M = 1 branch of
+ *     QQMatmul, qqmm.cpp, with the global scale of w kept).
  * fp32 accumulation, bf16 (RNE) output.  `workspace` must hold
  * bsfp_qmm_workspace_bytes(...) bytes (16-byte aligned) and is overwritten.
  * x and y must be 16-byte aligned, w's scales and biases 4-byte aligned.

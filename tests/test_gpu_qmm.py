@@ -88,6 +88,37 @@ def test_mxfp4_config_weight_only_full(oracle_mod, bsfp, M):
     check_wonly(oracle_mod, bsfp, x, oracle_mod.quantize(1, w))
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_qq_decode_rows(oracle_mod, bsfp, mode, M):
+    """M <= 8 runs the qq product as a GEMV on the exactly dequantized x (the
+    qq decode path); same contract as the GEMM: alpha at every M."""
+    x = S.generic((M, 2048), 1.0, seed=800 + M, stream=mode)
+    w = S.generic((1000, 2048), 0.02, seed=801 + mode)
+    check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_mxfp4_config_qq_decode(oracle_mod, bsfp, M):
+    check_qq(oracle_mod, bsfp, S.mxfp4_activations(M), oracle_mod.quantize(1, S.mxfp4_weights()))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_qq_decode_and_gemm_paths_agree(oracle_mod, bsfp, mode):
+    """Rows 0..7 of a 9-row qq product (GEMM path) against the same 8 rows
+    alone (decode path): both within tolerance of each other.  NVFP4's g_x
+    comes from the whole x, so the 9th row is a copy of row 0 (same amax)."""
+    o = oracle_mod
+    x = S.generic((8, 1024), 1.0, seed=900, stream=mode)
+    x9 = np.concatenate([x, x[:1]], axis=0)
+    w = S.generic((600, 1024), 0.02, seed=901)
+    qd = oracle_to_dev(bsfp, o, o.quantize(mode, w))
+    a = o.bf16_to_f32(from_dev(bsfp.qmm(to_dev(x), qd, act="same"))).astype(np.float64)
+    c = o.bf16_to_f32(from_dev(bsfp.qmm(to_dev(x9), qd, act="same"))[:8]).astype(np.float64)
+    _, den, _, _ = o.matmul_qq(x, o.quantize(mode, w))
+    assert np.max(np.abs(a - c) / den) <= 2 * QQ_TOL
+
+
 def _sampled_qq(o, b, M, N, K, seed, n_rows=8, n_pairs=2048, x=None, w=None):
     if x is None:
         x, w = S.nvfp4_prefill(M=M, N=N, K=K, seed=seed)
