@@ -30,14 +30,16 @@
 //   would leave a small last round on the CUs, the output columns of that
 //   round go to a second launch with 128 x 64 tiles.
 //
-// gemm_mx_kernel -- MXFP4 x MXFP4 on the CDNA4 block-scaled MFMA
+// gemm_mxl_kernel -- MXFP4 x MXFP4 on the CDNA4 block-scaled MFMA
 //   v_mfma_scale_f32_32x32x64_f8f6f4: both operands stay 4-bit, and each
 //   lane hands the MFMA the E8M0 scale of the 32 k-values it holds, which is
-//   exactly one MXFP4 group.  No dequantization at all.
+//   exactly one MXFP4 group.  No dequantization at all.  Operand rows are
+//   staged through LDS in 256-K units with coalesced buffer-to-LDS copies.
 //
 // fp32 accumulation, bf16 round-to-nearest-even output, rows and columns
 // beyond M / N clamped on load and masked on store.
 #include <algorithm>
+#include <atomic>
 
 #include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
@@ -45,8 +47,6 @@
 namespace bsfp {
 
 namespace {
-
-constexpr int kThreads = 256;
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -414,87 +414,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     }
 }
 
-// MXFP4 x MXFP4 on the block-scaled MFMA.  Operands come straight from the
-// packed codes in global memory (L2-resident across the tiles that share
-// them), one K step (64) ahead.
-template <int WMT, int WNT>
-__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
-    const uint32_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-    const uint32_t* __restrict__ wc, const uint8_t* __restrict__ wsc, int M, int N, int K,
-    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, l32 = lane & 31;
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * 64 * WMT + wm * 32 * WMT, n0 = tn * 64 * WNT + wn * 32 * WNT;
-
-  int64_t mr[WMT], nr[WNT];
-#pragma unroll
-  for (int i = 0; i < WMT; ++i) mr[i] = min(m0 + 32 * i + l32, M - 1);
-#pragma unroll
-  for (int j = 0; j < WNT; ++j) nr[j] = min(n0 + 32 * j + l32, N - 1);
-
-  uint4 an[WMT], bn[WNT];
-  uint32_t asn[WMT], bsn[WNT];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < WMT; ++i) {
-      an[i] = *reinterpret_cast<const uint4*>(xc + mr[i] * (K / 8) + k0 / 8 + 4 * h);
-      asn[i] = xs[mr[i] * (K / 32) + k0 / 32 + h];
-    }
-#pragma unroll
-    for (int j = 0; j < WNT; ++j) {
-      bn[j] = *reinterpret_cast<const uint4*>(wc + nr[j] * (K / 8) + k0 / 8 + 4 * h);
-      bsn[j] = wsc[nr[j] * (K / 32) + k0 / 32 + h];
-    }
-  };
-
-  f32x16_t acc[WMT][WNT];
-#pragma unroll
-  for (int i = 0; i < WMT; ++i)
-#pragma unroll
-    for (int j = 0; j < WNT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    uint4 ac[WMT], bc[WNT];
-    uint32_t asc[WMT], bsc[WNT];
-#pragma unroll
-    for (int i = 0; i < WMT; ++i) { ac[i] = an[i]; asc[i] = asn[i]; }
-#pragma unroll
-    for (int j = 0; j < WNT; ++j) { bc[j] = bn[j]; bsc[j] = bsn[j]; }
-    if (k0 + 64 < K) load(k0 + 64);
-#pragma unroll
-    for (int i = 0; i < WMT; ++i) {
-      const i32x8_t av = {(int)ac[i].x, (int)ac[i].y, (int)ac[i].z, (int)ac[i].w, 0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) {
-        const i32x8_t bv = {(int)bc[j].x, (int)bc[j].y, (int)bc[j].z, (int)bc[j].w, 0, 0, 0, 0};
-        // formats 4/4: FP4 E2M1 for both operands; scales: E8M0 byte 0
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[i][j], 4, 4, 0, (int)asc[i], 0, (int)bsc[j]);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < WMT; ++i)
-#pragma unroll
-    for (int j = 0; j < WNT; ++j) {
-      const int n = n0 + 32 * j + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r]);
-      }
-    }
-}
-
-// Launch of gemm_dq_kernel on the output columns [n0, n0 + n) of y (weight
-// rows n0 .. n0 + n - 1), with the given launch events.
 template <int DEC, int WGM, int WGN, int WMT, int WNT>
 void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int n,
                const float* g1, const float* g2, uint16_t* y, hipStream_t s, hipEvent_t ev0,
@@ -562,15 +481,312 @@ hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float
   return run_dq_big<DEC>(A, M, w, g1, g2, y, s);
 }
 
+// MXFP4 x MXFP4 staged through LDS.  A workgroup of WM x WN x KS waves owns
+// a BM x BN output tile (BM = 32 WMT WM, BN = 32 WNT WN); each of its KS
+// k-groups walks its own share of the 256-K units and the partial tiles are
+// summed through LDS at the end in a fixed order.
+//
+// A stage holds one unit of the group's BM + BN operand rows: 128 code bytes
+// and 8 scale bytes per row.  Every stage load is a 1 KB buffer-to-LDS copy of
+// 8 whole rows (16 bytes per lane) or a 256-byte copy of 32 rows' scales, so
+// global reads are contiguous 128-byte row segments; the MFMA layout (lane
+// = row, one 16-byte block pair per lane) is then read from LDS.  The 16-byte
+// slot of piece p in row r is p ^ ((r >> 1) & 7), which keeps every 16 lanes
+// of a ds_read_b128 on distinct banks.  Same unit K order as the register
+// kernel above: half h takes pieces 4h .. 4h+3, op_sel picks the scale byte.
+// The last, partial unit loads only its 2J pieces (the rest come back as
+// zeros) and takes its scales, masked to the valid blocks, straight from
+// memory.  Three stages rotate with one barrier per unit, as in the bf16 GEMM.
+template <int WM, int WN, int KS, int WMT, int WNT>
+struct MxlCfg {
+  static constexpr int GW = WM * WN;  // waves per k-group
+  static constexpr int NW = GW * KS;
+  static constexpr int BM = 32 * WMT * WM, BN = 32 * WNT * WN, R = BM + BN;
+  static constexpr int CODE_B = R * 128, GROUP_B = R * 136;
+  static constexpr int STAGE_B = KS * GROUP_B;
+  static constexpr int CIW = R / 8 / GW, SIW = R / 32 / GW;  // loads per wave per stage
+  static constexpr int LDS = 3 * STAGE_B;
+  static_assert(R % (32 * GW) == 0, "whole scale loads per wave");
+  static_assert((KS - 1) * GW * WMT * WNT * 4096 <= LDS, "reduction fits the ring");
+};
+
+template <int WM, int WN, int KS, int WMT, int WNT>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
+    const uint32_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+    const uint32_t* __restrict__ wc, const uint8_t* __restrict__ wsc, int M, int N, int K,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n, int units_per_split) {
+  using C = MxlCfg<WM, WN, KS, WMT, WNT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int kOff = 0x40000000;  // beyond every window: loads return 0
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int ks = wave / C::GW, wg = wave % C::GW;
+  const int wm = wg / WN, wn = wg % WN;
+  const int h = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int rows_m = min(C::BM, M - m0), rows_n = min(C::BN, N - n0);
+  const int cb = K / 2, sb = K / 32;
+  const rsrc_t rxc = make_rsrc(reinterpret_cast<const uint8_t*>(xc) + (int64_t)m0 * cb,
+                               (int64_t)rows_m * cb);
+  const rsrc_t rxs = make_rsrc(xs + (int64_t)m0 * sb, (int64_t)rows_m * sb);
+  const rsrc_t rwc = make_rsrc(reinterpret_cast<const uint8_t*>(wc) + (int64_t)n0 * cb,
+                               (int64_t)rows_n * cb);
+  const rsrc_t rws = make_rsrc(wsc + (int64_t)n0 * sb, (int64_t)rows_n * sb);
+
+  const int nfull = K / 256, tailJ = (K % 256) / 64;
+  const int nunits = nfull + (tailJ ? 1 : 0);
+  const int u0 = ks * units_per_split;
+  const int u_end = min(nunits, u0 + units_per_split);
+
+  // this wave's share of a stage: code loads s (rows 8 sg .. 8 sg + 7 of the
+  // group's A-then-B rows, sg = wg CIW + s) and scale loads (32 rows each)
+  int c_off[C::CIW], c_piece[C::CIW];
+#pragma unroll
+  for (int s = 0; s < C::CIW; ++s) {
+    const int row = 8 * (wg * C::CIW + s) + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    const int r = row < C::BM ? row : row - C::BM;
+    c_off[s] = r * cb + 16 * piece;
+    c_piece[s] = piece;
+  }
+  int s_off[C::SIW];
+#pragma unroll
+  for (int s = 0; s < C::SIW; ++s) {
+    const int row = 32 * (wg * C::SIW + s) + (lane >> 1);
+    const int r = row < C::BM ? row : row - C::BM;
+    s_off[s] = r * sb + 4 * (lane & 1);
+  }
+  auto group_base = [&](int slot) { return lds + slot * C::STAGE_B + ks * C::GROUP_B; };
+
+  auto load_stage = [&](int t, int slot) {
+    const int u = u0 + t;
+    const bool valid = u < u_end, tail = u == nfull;
+    uint8_t* base = group_base(slot);
+    const int uo = valid ? u * 128 : kOff;
+#pragma unroll
+    for (int s = 0; s < C::CIW; ++s) {
+      const bool isA = 8 * (wg * C::CIW + s) < C::BM;  // wave-uniform
+      const int off = c_off[s] + uo + ((tail && c_piece[s] >= 2 * tailJ) ? kOff : 0);
+      buffer_load_lds16(isA ? rxc : rwc, reinterpret_cast<uint4*>(base) + (wg * C::CIW + s) * 64,
+                        off, 0);
+    }
+    const int so = valid ? u * 8 : kOff;
+#pragma unroll
+    for (int s = 0; s < C::SIW; ++s) {
+      const bool isA = 32 * (wg * C::SIW + s) < C::BM;
+      buffer_load_lds4(isA ? rxs : rws, base + C::CODE_B + (wg * C::SIW + s) * 256,
+                       s_off[s] + so, 0);
+    }
+  };
+
+  f32x16_t acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  constexpr bool kSplitAcc = WMT * WNT == 1;
+  f32x16_t acc2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
+
+  int arow[WMT], brow[WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i) arow[i] = wm * 32 * WMT + 32 * i + l32;
+#pragma unroll
+  for (int j = 0; j < WNT; ++j) brow[j] = C::BM + wn * 32 * WNT + 32 * j + l32;
+
+  // Scales of the last, partial unit (pieces 4h + q < 2J; the others load
+  // out of range as 0, their codes being zero, or stale and then scaled below
+  // fp32's range): a few bytes per lane, fetched in the first stage step so
+  // their latency is long hidden when the unit comes up (fetched in the loop:
+  // a value loaded before it would make the compiler wait for every load in
+  // flight at the loop's entry).
+  uint32_t ta[WMT][4], tb[WNT][4];
+  auto load_tail_scales = [&]() {
+    const bool mine = tailJ && u0 < u_end && u_end == nunits;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool v = mine && 4 * h + q < 2 * tailJ;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int r = min(arow[i], rows_m - 1);
+        ta[i][q] = __builtin_amdgcn_raw_buffer_load_b8(
+            rxs, v ? r * sb + nfull * 8 + 4 * h + q : kOff, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const int r = min(brow[j] - C::BM, rows_n - 1);
+        tb[j][q] = __builtin_amdgcn_raw_buffer_load_b8(
+            rws, v ? r * sb + nfull * 8 + 4 * h + q : kOff, 0, 0);
+      }
+    }
+  };
+
+  auto compute = [&](int t, int slot) {
+    const int u = u0 + t;
+    if (u >= u_end) return;
+    const uint8_t* base = group_base(slot);
+    uint32_t sa[WMT], sw[WNT];
+    if (u != nfull) {
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+        sa[i] = *reinterpret_cast<const uint32_t*>(base + C::CODE_B + arow[i] * 8 + 4 * h);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+        sw[j] = *reinterpret_cast<const uint32_t*>(base + C::CODE_B + brow[j] * 8 + 4 * h);
+    } else {
+      // partial unit: the scale bytes fetched at the start (the empty asm
+      // keeps the combine, and so the wait for them, here rather than
+      // hoisted in front of the stage loop)
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(ta[i][q]));
+        sa[i] = ta[i][0] | (ta[i][1] << 8) | (ta[i][2] << 16) | (ta[i][3] << 24);
+      }
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(tb[j][q]));
+        sw[j] = tb[j][0] | (tb[j][1] << 8) | (tb[j][2] << 16) | (tb[j][3] << 24);
+      }
+    }
+    // all of the unit's LDS reads first, then its MFMAs back to back; a wave
+    // with a single tile alternates two accumulators (even / odd sub-steps)
+    // so consecutive MFMAs do not wait on each other
+    uint4 a[4][WMT], b[4][WNT];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+        a[q][i] = *reinterpret_cast<const uint4*>(
+            base + arow[i] * 128 + 16 * ((4 * h + q) ^ ((arow[i] >> 1) & 7)));
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+        b[q][j] = *reinterpret_cast<const uint4*>(
+            base + brow[j] * 128 + 16 * ((4 * h + q) ^ ((brow[j] >> 1) & 7)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto sub = [&](auto qc) {
+      constexpr int Q = decltype(qc)::value;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const i32x8_t av = {(int)a[Q][i].x, (int)a[Q][i].y, (int)a[Q][i].z, (int)a[Q][i].w,
+                            0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+          const i32x8_t bv = {(int)b[Q][j].x, (int)b[Q][j].y, (int)b[Q][j].z, (int)b[Q][j].w,
+                              0, 0, 0, 0};
+          f32x16_t& c = (kSplitAcc && (Q & 1)) ? acc2 : acc[i][j];
+          // formats 4/4: FP4 E2M1 for both operands; op_sel picks the E8M0 byte
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, Q, (int)sa[i], Q,
+                                                              (int)sw[j]);
+        }
+      }
+    };
+    sub(std::integral_constant<int, 0>{});
+    sub(std::integral_constant<int, 1>{});
+    sub(std::integral_constant<int, 2>{});
+    sub(std::integral_constant<int, 3>{});
+  };
+
+  // every wave runs the same number of stages (units_per_split); a k-group
+  // past its last unit loads out of range and skips the MFMAs
+  const int nst = units_per_split;
+  load_stage(0, 0);
+  if (nst > 1) load_stage(1, 1);
+  for (int t = 0; t < nst; ++t) {
+    if (t + 1 < nst) wait_vmem_le<C::CIW + C::SIW>();
+    else wait_vmem();
+    __syncthreads();
+    if (t + 2 < nst) load_stage(t + 2, (t + 2) % 3);
+    if (t == 0) load_tail_scales();
+    compute(t, t % 3);
+  }
+
+  if (kSplitAcc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][0][r] += acc2[r];
+  }
+
+  if (KS > 1) {
+    __syncthreads();  // every wave is done reading the ring
+    if (ks > 0) {
+      float* dst = reinterpret_cast<float*>(lds) + (size_t)((ks - 1) * C::GW + wg) * WMT * WNT * 1024;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * WNT + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+    for (int q = 1; q < KS; ++q) {
+      const float* src = reinterpret_cast<const float*>(lds) + (size_t)((q - 1) * C::GW + wg) * WMT * WNT * 1024;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * WNT + j) * 16 + r) * 64 + lane];
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int n = n0 + wn * 32 * WNT + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 32 * WMT + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+      }
+    }
+}
+
+template <int WM, int WN, int KS, int WMT, int WNT>
+hipError_t launch_mxl(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,
+                      uint16_t* y, hipStream_t s) {
+  using C = MxlCfg<WM, WN, KS, WMT, WNT>;
+  const int N = (int)w.rows, K = (int)w.cols;
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int nunits = (K + 255) / 256;
+  const int ups = (nunits + KS - 1) / KS;
+  if ((size_t)C::LDS > (size_t)device_max_lds()) return hipErrorInvalidConfiguration;
+  if (C::LDS > 64 * 1024) {
+    // opt in to the large LDS allocation, once per device
+    static std::atomic<bool> granted[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!granted[dev].load(std::memory_order_relaxed)) {
+      const hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+      if (e != hipSuccess) return e;
+      granted[dev].store(true, std::memory_order_relaxed);
+    }
+  }
+  launch_main(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT>, dim3(tiles_m * tiles_n), dim3(64 * C::NW),
+              (uint32_t)C::LDS, s, xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m,
+              tiles_n, ups);
+  return hipGetLastError();
+}
+
 hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,
                   uint16_t* y, hipStream_t s) {
-  constexpr int WMT = 1, WNT = 1;
-  const int N = (int)w.rows, K = (int)w.cols;
-  const int tiles_m = (M + 64 * WMT - 1) / (64 * WMT);
-  const int tiles_n = (N + 64 * WNT - 1) / (64 * WNT);
-  launch_main(&gemm_mx_kernel<WMT, WNT>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
-                     xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m, tiles_n);
-  return hipGetLastError();
+  // few rows: one 32 x 32 tile per workgroup with K split over 4 waves, so
+  // the N / 32 workgroups still carry 4 waves each; otherwise 128 x 128 tiles
+  // on 8 waves (64 x 32 per wave)
+  if (M <= 64) return launch_mxl<1, 1, 4, 1, 1>(xc, xs, M, w, y, s);
+  return launch_mxl<2, 4, 1, 2, 1>(xc, xs, M, w, y, s);
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
