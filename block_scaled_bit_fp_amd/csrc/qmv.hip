@@ -301,15 +301,23 @@ size_t fast_lds_bytes(int M, int NJ) {
 // out before the first weight loads and the LDS writes wait only for them.
 // Unit (m, c, u) holds x[m, 32c + 8u .. + 7] (affine: pairs reordered as the
 // nibble decode produces them); chunks past the row end are zero, so they
-// contribute nothing.  Each thread owns units tid + i * blockDim, i < kXU.
+// contribute nothing.  Each thread owns units tid + i * blockDim, i < XU
+// (kXU, or 8 for the 512-thread variants below).
 constexpr int kXU = 4;
 
+// Rows of x per launch above 2 need more registers per lane: those variants
+// run 512-thread workgroups (256 VGPRs), two per CU, staging 8 units of x per
+// thread (the same 64 KB of x at most).
+template <int MAXM> constexpr int fast_threads() { return MAXM > 2 ? 512 : 1024; }
+template <int MAXM> constexpr int fast_xu() { return MAXM > 2 ? 8 : kXU; }
+
+template <int XU>
 __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int M, int K,
-                                             int NJ, uint4 (&xr)[kXU]) {
+                                             int NJ, uint4 (&xr)[XU]) {
   const int cpr = K / 32;
   const int units = M * NJ * 128;
 #pragma unroll
-  for (int i = 0; i < kXU; ++i) {
+  for (int i = 0; i < XU; ++i) {
     const int b = threadIdx.x + i * blockDim.x;
     xr[i] = make_uint4(0u, 0u, 0u, 0u);
     if (b < units) {
@@ -321,12 +329,12 @@ __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int
   }
 }
 
-template <bool AFF>
-__device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[kXU],
+template <bool AFF, int XU>
+__device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[XU],
                                               uint4* __restrict__ xp, float* __restrict__ xs) {
   const int units = M * NJ * 128;
 #pragma unroll
-  for (int i = 0; i < kXU; ++i) {
+  for (int i = 0; i < XU; ++i) {
     const int b = threadIdx.x + i * blockDim.x;
     if (b < units) {  // units % 4 == 0: the 4 threads of a chunk agree
       const int m = b / (NJ * 128);
@@ -371,7 +379,7 @@ int block_scale_bytes(int R, int K) {
 //   so that the next
 //   block's scales are fetched only after this block's are in LDS.
 template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
-__global__ __launch_bounds__(1024) void qmv_fast_kernel(
+__global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
     const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y, int NJ, int nblocks) {
@@ -463,7 +471,7 @@ __global__ __launch_bounds__(1024) void qmv_fast_kernel(
 
   // x loads first, then the first PJ steps of weights; staging x into LDS
   // then waits only for the x loads (loads complete in issue order).
-  uint4 xr[kXU];
+  uint4 xr[fast_xu<MAXM>()];
   stage_x_load(x, M, K, NJ, xr);
   Chunk ring[PJ][R];
   int pf = 0, jf = 0;  // next step to fetch
@@ -651,20 +659,22 @@ struct FastShape {
   size_t lds;
 };
 
-template <int MODE, int R, bool SLDS>
+template <int MODE, int MAXM, int R, bool SLDS>
 FastShape fast_shape(int M, int K, int NJ, int64_t N) {
+  constexpr int kMaxW = fast_threads<MAXM>() / 64, kXu = fast_xu<MAXM>();
+  constexpr int kPerCu = 1024 / fast_threads<MAXM>();  // workgroups per CU
   const int cus = device_cu_count();
   const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
   const int units = M * NJ * 128;
-  const int min_wpg = std::max(1, (units + kXU * 64 - 1) / (kXU * 64));
-  const int64_t grid = std::min<int64_t>(cus, nblocks);
-  const int64_t passes = std::max<int64_t>(1, (nblocks + grid * 16 - 1) / (grid * 16));
+  const int min_wpg = std::max(1, (units + kXu * 64 - 1) / (kXu * 64));
+  const int64_t grid = std::min<int64_t>((int64_t)kPerCu * cus, nblocks);
+  const int64_t passes = std::max<int64_t>(1, (nblocks + grid * kMaxW - 1) / (grid * kMaxW));
   const int wpg = (int)std::min<int64_t>(
-      16, std::max<int64_t>(min_wpg, (nblocks + grid * passes - 1) / (grid * passes)));
+      kMaxW, std::max<int64_t>(min_wpg, (nblocks + grid * passes - 1) / (grid * passes)));
   size_t lds = fast_lds_bytes<MODE>(M, NJ) +
                (SLDS ? (size_t)wpg * block_scale_bytes<MODE>(R, K) : 0);
   const size_t half = (size_t)device_max_lds() / 2 + 16;
-  if (grid == cus && wpg <= 8 && lds < half) lds = half;
+  if (kPerCu == 1 && grid == cus && wpg <= 8 && lds < half) lds = half;
   return FastShape{(int)grid, wpg, lds};
 }
 
@@ -673,7 +683,7 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const fl
                        uint16_t* y, int NJ, hipStream_t s) {
   const int64_t N = w.rows;
   const int K = (int)w.cols;
-  const FastShape sh = fast_shape<MODE, R, SLDS>(M, K, NJ, N);
+  const FastShape sh = fast_shape<MODE, MAXM, R, SLDS>(M, K, NJ, N);
   const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
   // opt in to the large LDS allocation (160 KB on gfx950), once per device
   // and size
@@ -693,7 +703,7 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const fl
   return hipGetLastError();
 }
 
-// The staged x (kXU units per thread) is limited to 64 KB; the per-wave
+// The staged x (XU units per thread) is limited to 64 KB; the per-wave
 // scale areas come on top, up to the device's per-workgroup LDS limit.
 constexpr size_t kFastXLdsMax = 64 * 1024;
 
@@ -712,7 +722,7 @@ bool slds_ok(int K, int NJ, int M, int64_t N) {
   const int sarea = block_scale_bytes<MODE>(R, K) / (MODE == BSFP_AFFINE ? 2 : 1);
   const int srb = sarea / (2 * R);
   if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || kRing / R > NJ) return false;
-  return fast_shape<MODE, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
+  return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
 }
 
 template <int MODE>
