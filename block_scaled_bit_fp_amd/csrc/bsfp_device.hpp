@@ -153,6 +153,88 @@ __device__ __forceinline__ float dpp_sum32(float v) {
   return v;
 }
 
+// ------------------------------------------- activation quantize-dequantize
+
+// Byte SEL of w (two E2M1 codes) times the fp32 scale s, as a bf16 pair.
+// The products are exact in fp32 and, for E4M3 or power-of-two scales, in
+// bf16 as well, so the rounding in the pack never changes a value.
+template <int SEL>
+__device__ __forceinline__ uint32_t dq_pair_bf16(uint32_t w, float s) {
+  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return pack_bf16x2(v.x * s, v.y * s);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// NVFP4 quantize of 8 bf16 values followed by exact dequantization without
+// the global scale g: E2M1(code) * E4M3(S) as bf16.  The 8 values are half of
+// a 16-value group whose other half sits in lane ^ 1 (both lanes call this).
+// Codes and S are those of the NVFP4 quantizer with global scale g.
+__device__ __forceinline__ uint4 qdq_nvfp4_half_bf16(const uint4 xv, float g) {
+#pragma clang fp contract(off)
+  float f[8];
+  unpack8(xv, f);
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+  a = team_max<2>(a);
+  uint32_t S = 0;
+  float d = 0.0f;
+  if (g != 0.0f) {
+    S = e4m3_encode(a / (6.0f * g));
+    d = e4m3_decode(S) * g;
+  }
+  uint4 o = {0u, 0u, 0u, 0u};
+  if (d != 0.0f) {
+    const float inv = 1.0f / d;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
+    const uint32_t w = e2m1_pack8(v);
+    const float sf = e4m3_decode(S);
+    o.x = dq_pair_bf16<0>(w, sf);
+    o.y = dq_pair_bf16<1>(w, sf);
+    o.z = dq_pair_bf16<2>(w, sf);
+    o.w = dq_pair_bf16<3>(w, sf);
+  }
+  return o;
+}
+
+// MXFP4 quantize of 8 bf16 values followed by exact dequantization:
+// E2M1(code) * 2^e as bf16 (exact for the exponents a bf16 input can
+// produce).  The 8 values are a quarter of a 32-value group spread over 4
+// adjacent lanes (all four call this).
+__device__ __forceinline__ uint4 qdq_mxfp4_quarter_bf16(const uint4 xv) {
+#pragma clang fp contract(off)
+  float f[8];
+  unpack8(xv, f);
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+  a = team_max<4>(a);
+  // floor(log2 a) = biased exponent - 127 for normal a; subnormal or zero a
+  // gives an exponent below -128, which the clamp maps to -127
+  const int be = (int)(__float_as_uint(a) >> 23);
+  const int e = max(be - 129, -127);
+  const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
+  const uint32_t w = e2m1_pack8(v);
+  const float sc = ldexpf(1.0f, e);  // 2^e, subnormal for e = -127
+  uint4 o;
+  o.x = dq_pair_bf16<0>(w, sc);
+  o.y = dq_pair_bf16<1>(w, sc);
+  o.z = dq_pair_bf16<2>(w, sc);
+  o.w = dq_pair_bf16<3>(w, sc);
+  return o;
+}
+
 // ---------------------------------------------------------------- buffers
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

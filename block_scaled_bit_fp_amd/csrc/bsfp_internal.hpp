@@ -66,6 +66,13 @@ hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s
 // path passes g_x there).
 hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
                       hipStream_t s, const float* g2 = nullptr);
+// qq decode GEMV: x is quantized with w's format (NVFP4: global scale from
+// x's amax when w has one) while the GEMV stages it, and the products run on
+// its exact dequantization, with alpha = g_x * g_w on the output.  Applies
+// when qmv_qx_fusable(M, w) (x fits the GEMV's LDS copy, 1 <= M <= 8).
+bool qmv_qx_fusable(int M, const bsfp_qtensor& w);
+hipError_t launch_qmv_qx(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
+                         hipStream_t s);
 
 // ---- qmm (qmm.hip)
 size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act);

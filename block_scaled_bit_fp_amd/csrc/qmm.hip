@@ -825,7 +825,10 @@ hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int
     // qq decode: x is quantized with w's mode and dequantized exactly to bf16
     // (E2M1 * E4M3 and E2M1 * 2^e fit bf16), then the GEMV runs on it with
     // the output scaled by alpha = g_x * g_w (NVFP4 with a global scale on w)
-    // -- the same product as the GEMM path, at every M.
+    // -- the same product as the GEMM path, at every M.  When x fits the
+    // GEMV's LDS copy, the GEMV does all of it in one launch; otherwise the
+    // quantize-dequantize runs first into the workspace.
+    if (qmv_qx_fusable(M, w)) return launch_qmv_qx(x, M, w, y, s);
     if (w.mode == BSFP_NVFP4) {
       float* amax = reinterpret_cast<float*>(ws);
       float* gx = amax + 1;

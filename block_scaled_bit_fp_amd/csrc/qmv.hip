@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(
   const int lt = threadIdx.x % kTeam;
   const int64_t cpr = K / 32;                 // chunks per row
   const int ipr = (nch + kTeam - 1) / kTeam;  // items per lane per row and slice
-  const float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
+  float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
 
   // rows of this team: gt, gt + T, gt + 2T, ... (T = teams in the grid)
   const int64_t gt = (int64_t)blockIdx.x * kTeams + team;
@@ -329,9 +329,10 @@ __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int
   }
 }
 
-template <bool AFF, int XU>
+template <bool AFF, int XU, int QXMODE>
 __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[XU],
-                                              uint4* __restrict__ xp, float* __restrict__ xs) {
+                                              uint4* __restrict__ xp, float* __restrict__ xs,
+                                              float gq) {
   const int units = M * NJ * 128;
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
@@ -340,7 +341,10 @@ __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[X
       const int m = b / (NJ * 128);
       const int rem = b - m * NJ * 128;
       const int c = rem >> 2, u = rem & 3;
-      const uint4 v = xr[i];
+      uint4 v = xr[i];
+      // qq: x quantized with the weights' format and dequantized exactly
+      if constexpr (QXMODE == BSFP_NVFP4) v = qdq_nvfp4_half_bf16(v, gq);
+      if constexpr (QXMODE == BSFP_MXFP4) v = qdq_mxfp4_quarter_bf16(v);
       uint4 o = v;
       if constexpr (AFF) {
         o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
@@ -378,11 +382,18 @@ int block_scale_bytes(int R, int K) {
 //   row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and PJ <= NJ,
 //   so that the next
 //   block's scales are fetched only after this block's are in LDS.
-template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
+// QX (qq decode): x is quantized with the weights' format while it is
+// staged and the products run on its exact dequantization; for NVFP4 with
+// qx_amax set, every workgroup takes the global activation scale
+// g_x = amax(x) / 2688 over the whole x it stages and folds it into the
+// output scale (without it, g_x = 1).
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
 __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y, int NJ, int nblocks) {
+    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y,
+    int NJ, int nblocks, int qx_amax) {
+  static_assert(!QX || MODE != BSFP_AFFINE, "qq needs a 4-bit float format");
   static_assert(!(SLDS && RAGGED), "staged scales need whole 32-chunk steps");
   constexpr bool AFF = (MODE == BSFP_AFFINE);
   constexpr int PJ = kRing / R;  // steps in flight
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
   const int nb_wg = nblocks > wg ? (nblocks - wg + G - 1) / G : 0;
   const int passes = wave_in_wg < nb_wg ? (nb_wg - wave_in_wg + wpg - 1) / wpg : 0;
   const int steps = passes * NJ;
-  const float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
+  float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
 
   // this wave's scale area (SLDS): [2R rows][srb] scales, then the biases
   const int sarea = 2 * R * srb;
@@ -486,7 +497,31 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
       }
     }
   }
-  stage_x_store<AFF>(M, NJ, xr, xp, xs);
+  float gq = 1.0f;
+  if constexpr (QX && MODE == BSFP_NVFP4) {
+    if (qx_amax) {
+      // max |x| over the staged x: per wave, then over the waves through the
+      // (not yet written) x area of LDS
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < fast_xu<MAXM>(); ++i) {
+        float f[8];
+        unpack8(xr[i], f);  // units past the end were loaded as zeros
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+      }
+      a = team_max<64>(a);
+      float* red = reinterpret_cast<float*>(xp);
+      if (lane == 0) red[wave_in_wg] = a;
+      __syncthreads();
+      a = red[0];
+      for (int w2 = 1; w2 < wpg; ++w2) a = fmaxf(a, red[w2]);
+      __syncthreads();
+      gq = a / 2688.0f;
+      g *= gq;
+    }
+  }
+  stage_x_store<AFF, fast_xu<MAXM>(), QX ? MODE : -1>(M, NJ, xr, xp, xs, gq);
   __syncthreads();
   if (steps == 0) return;
 
@@ -678,9 +713,9 @@ FastShape fast_shape(int M, int K, int NJ, int64_t N) {
   return FastShape{(int)grid, wpg, lds};
 }
 
-template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS>
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
 hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
-                       uint16_t* y, int NJ, hipStream_t s) {
+                       uint16_t* y, int NJ, hipStream_t s, int qx_amax) {
   const int64_t N = w.rows;
   const int K = (int)w.cols;
   const FastShape sh = fast_shape<MODE, MAXM, R, SLDS>(M, K, NJ, N);
@@ -692,14 +727,14 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const fl
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (sh.lds > 64 * 1024 && sh.lds > lds_granted[dev].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>),
+        reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
     if (e != hipSuccess) return e;
     lds_granted[dev].store(sh.lds, std::memory_order_relaxed);
   }
-  launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS>, dim3((unsigned)sh.grid),
+  launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX>, dim3((unsigned)sh.grid),
                      dim3(64 * sh.wpg), sh.lds, s, x, M, K, (int)N, w.codes, w.scales,
-                     w.biases, w.global_scale, g2, y, NJ, (int)nblocks);
+                     w.biases, w.global_scale, g2, y, NJ, (int)nblocks, qx_amax);
   return hipGetLastError();
 }
 
@@ -725,9 +760,9 @@ bool slds_ok(int K, int NJ, int M, int64_t N) {
   return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
 }
 
-template <int MODE>
+template <int MODE, bool QX = false>
 hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2, uint16_t* y,
-                hipStream_t s) {
+                hipStream_t s, int qx_amax = 0) {
   const int K = (int)w.cols;
   const int NJ = (int)((w.cols / 32 + 31) / 32);
   const bool ragged = (w.cols / 32) % 32 != 0;
@@ -737,25 +772,27 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
       const int64_t want = 8LL * device_cu_count();
       const int64_t N = w.rows;
       if (N >= 8 * want && slds_ok<MODE, 4>(K, NJ, M, N))
-        return launch_fast<MODE, 1, 4, false, true>(x, M, w, g2, y, NJ, s);
+        return launch_fast<MODE, 1, 4, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
       if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, M, N))
-        return launch_fast<MODE, 1, 2, false, true>(x, M, w, g2, y, NJ, s);
-      if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true>(x, M, w, g2, y, NJ, s);
-      if (slds_ok<MODE, 2>(K, NJ, M, N)) return launch_fast<MODE, 1, 2, false, true>(x, M, w, g2, y, NJ, s);
-      if (slds_ok<MODE, 4>(K, NJ, M, N)) return launch_fast<MODE, 1, 4, false, true>(x, M, w, g2, y, NJ, s);
-      if (ragged) return launch_fast<MODE, 1, 1, true, false>(x, M, w, g2, y, NJ, s);
-      return launch_fast<MODE, 1, 1, false, false>(x, M, w, g2, y, NJ, s);
+        return launch_fast<MODE, 1, 2, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      if (slds_ok<MODE, 2>(K, NJ, M, N)) return launch_fast<MODE, 1, 2, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      if (slds_ok<MODE, 4>(K, NJ, M, N)) return launch_fast<MODE, 1, 4, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      if (ragged) return launch_fast<MODE, 1, 1, true, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      return launch_fast<MODE, 1, 1, false, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
     }
     if (ragged) {
-      if (M == 2) return launch_fast<MODE, 2, 1, true, false>(x, M, w, g2, y, NJ, s);
-      if (M <= 4) return launch_fast<MODE, 4, 1, true, false>(x, M, w, g2, y, NJ, s);
-      return launch_fast<MODE, 8, 1, true, false>(x, M, w, g2, y, NJ, s);
+      if (M == 2) return launch_fast<MODE, 2, 1, true, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      if (M <= 4) return launch_fast<MODE, 4, 1, true, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+      return launch_fast<MODE, 8, 1, true, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
     }
-    if (M == 2) return launch_fast<MODE, 2, 1, false, false>(x, M, w, g2, y, NJ, s);
-    if (M <= 4) return launch_fast<MODE, 4, 1, false, false>(x, M, w, g2, y, NJ, s);
-    return launch_fast<MODE, 8, 1, false, false>(x, M, w, g2, y, NJ, s);
+    if (M == 2) return launch_fast<MODE, 2, 1, false, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+    if (M <= 4) return launch_fast<MODE, 4, 1, false, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
+    return launch_fast<MODE, 8, 1, false, false, QX>(x, M, w, g2, y, NJ, s, qx_amax);
   }
-  // x too large for one LDS copy: walk K in slices
+  // x too large for one LDS copy: walk K in slices (plain x only; callers
+  // check qmv_qx_fusable first)
+  if constexpr (QX) return hipErrorInvalidValue;
   if (M == 1) return run<MODE, 1>(x, M, w, g2, y, s);
   if (M == 2) return run<MODE, 2>(x, M, w, g2, y, s);
   if (M <= 4) return run<MODE, 4>(x, M, w, g2, y, s);
@@ -763,6 +800,23 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
 }
 
 }  // namespace
+
+bool qmv_qx_fusable(int M, const bsfp_qtensor& w) {
+  if (w.cols % 32 != 0 || w.cols >= (1 << 28) || w.rows >= (1 << 30) || M < 1 || M > 8)
+    return false;
+  const int NJ = (int)((w.cols / 32 + 31) / 32);
+  if (w.mode == BSFP_NVFP4) return fast_ok<BSFP_NVFP4>(M, NJ);
+  if (w.mode == BSFP_MXFP4) return fast_ok<BSFP_MXFP4>(M, NJ);
+  return false;
+}
+
+hipError_t launch_qmv_qx(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
+                         hipStream_t s) {
+  if (w.rows == 0) return hipGetLastError();
+  if (w.mode == BSFP_NVFP4)
+    return by_m<BSFP_NVFP4, true>(x, M, w, nullptr, y, s, w.global_scale ? 1 : 0);
+  return by_m<BSFP_MXFP4, true>(x, M, w, nullptr, y, s, 0);
+}
 
 hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
                       hipStream_t s, const float* g2) {

@@ -31,22 +31,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Byte SEL of w (two E2M1 codes) times the fp32 scale s, as a bf16 pair.
-// The products are exact in fp32 and, for E4M3 or power-of-two scales, in
-// bf16 as well, so the rounding in the pack never changes a value.
-template <int SEL>
-__device__ __forceinline__ uint32_t dq_pair_bf16(uint32_t w, float s) {
-  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-  return pack_bf16x2(v.x * s, v.y * s);
-}
-
-__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
-
 // ------------------------------------------------------------------ amax
 
 __global__ void amax_init_kernel(float* out) { *out = 0.0f; }
@@ -153,6 +137,10 @@ __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
   const float six_g = 6.0f * g;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
+    if constexpr (BF16) {
+      xhat[i] = qdq_nvfp4_half_bf16(x[i], g);
+      continue;
+    }
     float f[8];
     unpack8(x[i], f);
     float a = 0.0f;
@@ -172,20 +160,12 @@ __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
       const uint32_t w = e2m1_pack8(v);
-      if constexpr (BF16) {
-        const float sf = e4m3_decode(S);
-        o.x = dq_pair_bf16<0>(w, sf);
-        o.y = dq_pair_bf16<1>(w, sf);
-        o.z = dq_pair_bf16<2>(w, sf);
-        o.w = dq_pair_bf16<3>(w, sf);
-      } else {
-        const _Float16 sh = (_Float16)e4m3_decode(S);  // exact in fp16
-        const f16x2_t s2 = {sh, sh};
-        o.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
-        o.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
-        o.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
-        o.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
-      }
+      const _Float16 sh = (_Float16)e4m3_decode(S);  // exact in fp16
+      const f16x2_t s2 = {sh, sh};
+      o.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(w) * s2);
+      o.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(w) * s2);
+      o.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(w) * s2);
+      o.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(w) * s2);
     }
     xhat[i] = o;
   }
@@ -224,28 +204,8 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
 __global__ __launch_bounds__(kThreads) void quantize_dequant_mxfp4_bf16_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint4* __restrict__ xhat) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
-    float f[8];
-    unpack8(x[i], f);
-    float a = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
-    a = team_max<4>(a);
-    const int be = (int)(__float_as_uint(a) >> 23);
-    const int e = max(be - 129, -127);
-    const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
-    const uint32_t w = e2m1_pack8(v);
-    const float sc = ldexpf(1.0f, e);  // 2^e, subnormal for e = -127
-    uint4 o;
-    o.x = dq_pair_bf16<0>(w, sc);
-    o.y = dq_pair_bf16<1>(w, sc);
-    o.z = dq_pair_bf16<2>(w, sc);
-    o.w = dq_pair_bf16<3>(w, sc);
-    xhat[i] = o;
-  }
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride)
+    xhat[i] = qdq_mxfp4_quarter_bf16(x[i]);
 }
 
 // ------------------------------------------------------------------ affine

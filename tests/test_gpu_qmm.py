@@ -5,8 +5,12 @@ oracle's fp64 product (the pages' ~3e-3 relative bf16 tolerance against a
 dequantized f32 reference, "feat(quant): backend quantization capability
 table ...", 2026-09-29 update).  For the qq paths the dequantized operand
 products are exact on the MFMA and only fp32 summation order and the final
-bf16 rounding (<= 2^-9) remain, so they are also held to 2.2e-3.  At the full
-prefill size the oracle computes sampled outputs one by one."""
+bf16 rounding remain; the rounding is at most 2^-8 of |y|, and for the
+independent x and w draws used here |y| stays far below sum_k |a_k b_k|, so
+they are held to 2.2e-3.  (x and w from one random stream would make
+|y| ~ sum_k |a_k b_k| on matching rows and the rounding alone could reach
+3.9e-3 there.)  At the full prefill size the oracle computes sampled outputs
+one by one."""
 import numpy as np
 import pytest
 import torch
@@ -105,6 +109,22 @@ def test_qq_decode_rows(oracle_mod, bsfp, mode, M):
     qq decode path); same contract as the GEMM: alpha at every M."""
     x = S.generic((M, 2048), 1.0, seed=800 + M, stream=mode)
     w = S.generic((1000, 2048), 0.02, seed=801 + mode)
+    check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+def test_qq_decode_nvfp4_without_global_scale(oracle_mod, bsfp):
+    """NVFP4 weights without a global scale: x is quantized with g = 1 too."""
+    x = S.generic((3, 1024), 1.0, seed=810)
+    w = S.generic((500, 1024), 0.02, seed=811)
+    check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(2, w, use_global=False))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_qq_decode_x_beyond_gemv_lds(oracle_mod, bsfp, mode):
+    """8 rows of K = 8192 (128 KB of x) exceed the GEMV's LDS copy of x: the
+    quantize-dequantize runs as its own pass into the workspace first."""
+    x = S.generic((8, 8192), 1.0, seed=820 + mode)
+    w = S.generic((300, 8192), 0.02, seed=830)
     check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
 
 
