@@ -267,6 +267,20 @@ def matmul_wonly(x_bits: np.ndarray, w: QTensor):
     return matmul_f64(x, dequant_exact(w, with_g=True))
 
 
+def matmul_dense(x_bits: np.ndarray, w: QTensor, rows: Optional[np.ndarray] = None):
+    """Dense prefill path ("mlx: opt-in dense GEMM for nvfp4 prefill
+    (dequantise to bf16 above a row threshold)"): W dequantized to bf16 by
+    the dequantize rule (NVFP4 with its global scale, one rounding to bf16),
+    then y = x . W_bf16^T computed exactly.  Returns (y, denom); with `rows`,
+    the bf16 weights of those rows only (for sampled checks), as (W_bf16
+    rows in fp64) instead."""
+    Wb = bf16_to_f64(dequantize(w))
+    if rows is not None:
+        return Wb[np.asarray(rows, np.int64)]
+    x = bf16_to_f64(np.atleast_2d(x_bits))
+    return matmul_f64(x, Wb)
+
+
 def qq_operands(x_bits: np.ndarray, w: QTensor):
     """x quantized with W's mode; returns (qx, A = dq0(qx), B = dq0(W), alpha)."""
     qx = quantize(w.mode, np.atleast_2d(x_bits), use_global=(w.mode == NVFP4 and w.g is not None))

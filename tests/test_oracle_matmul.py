@@ -6,7 +6,10 @@
   weights (y = selected activations), which pin nibble order, scale indexing
   and the row mapping;
 - qq consistency: alpha * dq0(x) dq0(W)^T equals the product of the fully
-  dequantized operands (the pages' alpha = amax_x amax_w / (448*6)^2).
+  dequantized operands (the pages' alpha = amax_x amax_w / (448*6)^2);
+- the dense path (W rounded to bf16 first): equal to the weight-only product
+  where that rounding is exact, equal to a product over weights decoded and
+  rounded independently here, and within 2^-8 of the weight-only product.
 """
 import numpy as np
 import pytest
@@ -147,3 +150,41 @@ def test_norm_err(oracle_mod):
     e = o.norm_err(ybits, yref, den)
     assert e[0] == pytest.approx(0.0078125 / 4)
     assert e[1] == 0 and e[2] == 0 and np.isinf(e[3])
+
+
+def independent_bf16_weights(o, q):
+    """The dequantize rule without the oracle's codecs: the fp32 value
+    (E2M1 * E4M3 exact, times g rounded to fp32; affine fma(s, q, b) in one
+    fp32 rounding, exact in fp64 for these magnitudes), then fp32 -> bf16
+    nearest even (torch's conversion)."""
+    w = independent_dequant(o, q, with_g=False)
+    if q.mode == o.NVFP4 and q.g is not None:
+        w32 = w.astype(np.float32) * np.float32(q.g)
+    else:
+        w32 = w.astype(np.float32)
+    return torch.from_numpy(w32).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("use_global", [True, False])
+def test_dense_path_pins(oracle_mod, mode, use_global):
+    o = oracle_mod
+    if mode != o.NVFP4 and not use_global:
+        pytest.skip("the global scale exists for NVFP4 only")
+    M, N, K = 3, 40, 128
+    x = generic((M, K), 1.0, seed=40 + mode, stream=int(use_global))
+    w = generic((N, K), 0.02, seed=41 + mode)
+    q = o.quantize(mode, w, use_global=use_global) if mode == o.NVFP4 else o.quantize(mode, w)
+    yd, dd = o.matmul_dense(x, q)
+    yw, dw = o.matmul_wonly(x, q)
+    # independent decode and rounding
+    yi, _ = o.matmul_f64(bf16_f64(x), independent_bf16_weights(o, q))
+    assert np.array_equal(yd, yi)
+    # bf16 rounding of W is exact for MXFP4 and for NVFP4 without g
+    if mode == o.MXFP4 or (mode == o.NVFP4 and not use_global):
+        assert np.array_equal(yd, yw) and np.array_equal(dd, dw)
+    # within one bf16 rounding of the weights (relative 2^-8)
+    assert np.all(np.abs(yd - yw) <= 2.0 ** -8 * dw + 1e-300)
+    # the row selection returns the same weights
+    rows = np.array([0, 7, N - 1])
+    assert np.array_equal(o.matmul_dense(x, q, rows=rows), independent_bf16_weights(o, q)[rows])
