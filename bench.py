@@ -19,6 +19,11 @@ already resident in HBM:
               dequantized exactly, then the GEMV; alpha = g_x g_w)
   qmm_mx32 / qmm_mx512   MXFP4 qq GEMM on the scaled MFMA, W[5760,2880]
   qmm_affine  affine weight-only x[2048,5120] . W_up[25600,5120]^T
+  wonly_M / dense_M   NVFP4 weight-only X[M,5120] . W[25600,5120]^T at
+              M = 1134, 2048, 4096: the fused kernel (W decoded in registers)
+              and the dense prefill path (W dequantized to bf16 into one
+              reused scratch, then a dense bf16 GEMM); `dense_crossover` maps
+              their ratio
 
 The JSON line reports the headline metric: `value` is the sustained qmv GB/s
 of the 64-layer sweep (algorithmic bytes: packed codes + scales + biases +
@@ -188,11 +193,23 @@ def main():
     def st_qmm_affine():
         b.qmm(X_aff, q_up0, act="bf16", out=Y_aff)
 
+    # dense prefill path vs the fused weight-only kernel on the NVFP4 weights
+    dense_scratch = torch.empty(b.qmm_dense_scratch_bytes(INTER, HIDDEN), dtype=torch.uint8,
+                                device=dev)
+
+    def wonly(M):
+        return lambda: b.qmm(X_pf[M], q_pf, act="bf16", out=Y_pf[M])
+
+    def dense(M):
+        return lambda: b.qmm_dense(X_pf[M], q_pf, scratch=dense_scratch, out=Y_pf[M])
+
     stages = [("act_quant", st_act_quant), ("dequant", st_dequant), ("w_quant", st_w_quant),
               ("qmv_sweep", st_qmv_sweep), ("qmv_fp4", st_qmv_fp4), ("qqmm", qq(2048)),
               ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qq_decode", st_qq_decode),
               ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)),
               ("qmm_affine", st_qmm_affine)]
+    for M in (1134, 2048, 4096):
+        stages += [(f"wonly_{M}", wonly(M)), (f"dense_{M}", dense(M))]
     if args.only:
         keep = set(args.only.split(","))
         stages = [s for s in stages if s[0] in keep]
@@ -285,6 +302,15 @@ def main():
                 out[f"qmm_tflops_m{M}"] = round(2.0 * M * INTER * HIDDEN / (ms[key] * 1e-3) / 1e12, 1)
     if "qmm_affine" in ms:
         out["qmm_affine_tflops"] = round(2.0 * 2048 * INTER * HIDDEN / (ms["qmm_affine"] * 1e-3) / 1e12, 1)
+    cross = {}
+    for M in (1134, 2048, 4096):
+        if f"dense_{M}" in ms and f"wonly_{M}" in ms:
+            flop = 2.0 * M * INTER * HIDDEN
+            cross[str(M)] = {"dense_tflops": round(flop / (ms[f"dense_{M}"] * 1e-3) / 1e12, 1),
+                             "fused_tflops": round(flop / (ms[f"wonly_{M}"] * 1e-3) / 1e12, 1),
+                             "dense_over_fused": round(ms[f"wonly_{M}"] / ms[f"dense_{M}"], 3)}
+    if cross:
+        out["dense_crossover"] = cross
     if "qq_decode" in ms:
         out["qq_decode_gbs"] = round(fp4_bytes(INTER, HIDDEN, 16) / (ms["qq_decode"] * 1e-3) / 1e9, 1)
     if "qmm_mx32" in ms:  # HBM-bound size: weight + activation bytes per call

@@ -29,8 +29,8 @@ ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
 
 EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
-           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_time_next_launch",
-           "bsfp_last_error", "bsfp_version")
+           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_qmm_dense_scratch_bytes",
+           "bsfp_qmm_dense", "bsfp_time_next_launch", "bsfp_last_error", "bsfp_version")
 
 
 class QTensorDesc(C.Structure):
@@ -67,6 +67,8 @@ def lib():
             "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
             "bsfp_qmm_workspace_bytes": (C.c_size_t, [I32, I64, I64, I32]),
             "bsfp_qmm": (C.c_int, [P, I64, QP, I32, P, C.c_size_t, P, P]),
+            "bsfp_qmm_dense_scratch_bytes": (C.c_size_t, [I64, I64]),
+            "bsfp_qmm_dense": (C.c_int, [P, I64, QP, P, C.c_size_t, P, P]),
             "bsfp_time_next_launch": (C.c_int, [P, P]),
             "bsfp_last_error": (C.c_char_p, []),
             "bsfp_version": (C.c_char_p, []),
@@ -220,14 +222,42 @@ def qmm_workspace_bytes(mode: int, M: int, K: int, act: str = "bf16") -> int:
     return int(lib().bsfp_qmm_workspace_bytes(mode, M, K, ACT_SAME if act == "same" else ACT_BF16))
 
 
-def qmm(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
-        workspace: Optional[torch.Tensor] = None,
-        out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y[M, N] = x . dq(W)^T ('bf16') or alpha * dq0(q(x)) . dq0(W)^T ('same')."""
+def qmm_dense_scratch_bytes(rows: int, cols: int) -> int:
+    return int(lib().bsfp_qmm_dense_scratch_bytes(rows, cols))
+
+
+def qmm_dense(x: torch.Tensor, w: QuantizedTensor, scratch: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense prefill path: W dequantized to bf16 into `scratch` (one layer's
+    copy, caller-owned and reusable), then y = x . scratch^T."""
     x2 = _as_2d_bf16(x)
     M = x2.shape[0]
     if x2.shape[1] != w.cols:
         raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    need = qmm_dense_scratch_bytes(w.rows, w.cols)
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    d = w.desc()
+    _check(lib().bsfp_qmm_dense(_ptr(x2), M, C.byref(d), _ptr(scratch),
+                                scratch.numel() * scratch.element_size(), _ptr(out), _stream()))
+    return out
+
+
+def qmm(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
+        workspace: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None, dense_rows: Optional[int] = None,
+        scratch: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M, N] = x . dq(W)^T ('bf16') or alpha * dq0(q(x)) . dq0(W)^T ('same').
+    With dense_rows set, a 'bf16' call of at least that many rows takes the
+    dense path (qmm_dense, dequantizing into `scratch`); off by default."""
+    x2 = _as_2d_bf16(x)
+    M = x2.shape[0]
+    if x2.shape[1] != w.cols:
+        raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    if act != "same" and dense_rows is not None and M >= dense_rows:
+        return qmm_dense(x2, w, scratch=scratch, out=out)
     a = ACT_SAME if act == "same" else ACT_BF16
     need = int(lib().bsfp_qmm_workspace_bytes(w.mode, M, w.cols, a))
     if need and workspace is None:

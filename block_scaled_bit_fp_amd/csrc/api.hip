@@ -249,4 +249,37 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_
   return device_status(launch_qmm(x, M, *w, act, workspace, y, (hipStream_t)stream), "bsfp_qmm");
 }
 
+size_t bsfp_qmm_dense_scratch_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return (size_t)rows * (size_t)cols * 2;
+}
+
+bsfp_status bsfp_qmm_dense(const uint16_t* x, int64_t M, const bsfp_qtensor* w, void* scratch,
+                           size_t scratch_bytes, uint16_t* y, bsfp_stream stream) {
+  bsfp_status st = check_qtensor(w, "bsfp_qmm_dense");
+  if (st != BSFP_OK) return st;
+  if (M < 0) return fail(BSFP_ERR_ARG, "bsfp_qmm_dense: negative M");
+  if (M == 0 || w->rows == 0) return ok();
+  if (w->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmm_dense: K must be positive");
+  if (!x || !aligned16(x))
+    return fail(BSFP_ERR_ARG, "bsfp_qmm_dense: x is null or not 16-byte aligned");
+  if (!y || !aligned16(y))
+    return fail(BSFP_ERR_ARG, "bsfp_qmm_dense: y is null or not 16-byte aligned");
+  if (w->cols % 64)
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: K = %lld is not a multiple of 64",
+                (long long)w->cols);
+  if (M > (1 << 30) || w->rows > (1 << 30))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: M or N beyond 2^30");
+  if (w->cols > (1 << 22))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: K = %lld beyond 2^22",
+                (long long)w->cols);
+  const size_t need = bsfp_qmm_dense_scratch_bytes(w->rows, w->cols);
+  if (!scratch || scratch_bytes < need || !aligned16(scratch))
+    return fail(BSFP_ERR_ARG,
+                "bsfp_qmm_dense: scratch needs %zu bytes (16-byte aligned), got %zu", need,
+                scratch_bytes);
+  return device_status(launch_qmm_dense(x, M, *w, scratch, y, (hipStream_t)stream),
+                       "bsfp_qmm_dense");
+}
+
 }  // extern "C"

@@ -78,5 +78,7 @@ hipError_t launch_qmv_qx(const uint16_t* x, int M, const bsfp_qtensor& w, uint16
 size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act);
 hipError_t launch_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor& w, int act,
                       void* ws, uint16_t* y, hipStream_t s);
+hipError_t launch_qmm_dense(const uint16_t* x, int64_t M, const bsfp_qtensor& w, void* scratch,
+                            uint16_t* y, hipStream_t s);
 
 }  // namespace bsfp

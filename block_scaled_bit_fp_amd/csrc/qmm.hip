@@ -53,7 +53,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-enum { DEC_AFFINE = 0, DEC_MXFP4 = 1, DEC_NVFP4 = 2, DEC_NVFP4_F16 = 3 };
+enum { DEC_AFFINE = 0, DEC_MXFP4 = 1, DEC_NVFP4 = 2, DEC_NVFP4_F16 = 3, DEC_DENSE = 4 };
 
 // Expanded B operand of one MFMA (8 consecutive k of one weight row).
 struct Op8 {
@@ -232,9 +232,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   // for them is the explicit vmcnt before each step's barrier, so two steps
   // of loads stay in flight.  Every wave issues the same number of loads per
   // step, which makes that count exact for each wave.
+  // DEC_DENSE: B is a plain bf16 [N, K] matrix, staged like A ([BN][8]
+  // swizzled chunks), with no scales.
+  constexpr bool DENSE = DEC == DEC_DENSE;
   constexpr int A_U4 = BM * 8;          // [BM][8] 16-byte chunks, swizzled
-  constexpr int BC_U4 = BN * 2;         // [BN][2] 16-byte code chunks
-  constexpr int BS_U4 = BN / 4;         // [BN] scale dwords
+  constexpr int BC_U4 = DENSE ? BN * 8 : BN * 2;  // [BN][2] 16-byte code chunks
+  constexpr int BS_U4 = DENSE ? 0 : BN / 4;       // [BN] scale dwords
   constexpr int BB_U4 = (DEC == DEC_AFFINE) ? BN / 4 : 0;  // [BN] bias dwords
   constexpr int STAGE_U4 = A_U4 + BC_U4 + BS_U4 + BB_U4;
   __shared__ uint4 smem[3 * STAGE_U4];
@@ -259,12 +262,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   }
 
   // B codes: 16-byte piece p of the tile's step is row p / 2, half p % 2;
-  // each wave loads PPW consecutive pieces.
+  // each wave loads PPW consecutive pieces.  Dense B: BROWS rows per wave,
+  // like A.
   constexpr int PPW = 2 * BN / NW;
   constexpr int BC_LOADS = (PPW + 63) / 64;
-  static_assert(PPW * NW == 2 * BN && (PPW >= 64 ? PPW % 64 == 0 : 64 % PPW == 0),
+  static_assert(DENSE || (PPW * NW == 2 * BN && (PPW >= 64 ? PPW % 64 == 0 : 64 % PPW == 0)),
                 "code pieces split evenly over the waves");
-  const rsrc_t rc = make_rsrc(codes + (int64_t)n_base * (K / 8), (int64_t)rows_n * (K / 2));
+  constexpr int BROWS = BN / NW;
+  static_assert(!DENSE || BROWS % 8 == 0, "each wave loads whole 8-row LDS blocks of B");
+  const rsrc_t rc = DENSE ? make_rsrc(reinterpret_cast<const uint16_t*>(codes) + (int64_t)n_base * K,
+                                      (int64_t)rows_n * K * 2)
+                          : make_rsrc(codes + (int64_t)n_base * (K / 8), (int64_t)rows_n * (K / 2));
+  int b_off[DENSE ? BROWS / 8 : 1];
+  if constexpr (DENSE) {
+#pragma unroll
+    for (int s = 0; s < BROWS / 8; ++s) {
+      const int r = wave * BROWS + s * 8 + (lane >> 3);
+      b_off[s] = r * K * 2 + swz(r, lane & 7) * 16;
+    }
+  }
   // B scales (and affine biases): one dword per tile row and step, read by
   // BN / NW lanes of each wave.  NVFP4 needs 4 bytes per row and step (four
   // E4M3 blocks of 16); MXFP4 and affine need 2, taken from the aligned dword
@@ -274,8 +290,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   constexpr int SROWS = BN / NW;  // scale rows per wave
   static_assert(SROWS <= 64, "one scale load per wave and array");
   const int srb = (K / gsz) * sbytes;  // scale bytes per weight row
-  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * srb,
-                              (int64_t)rows_n * srb);
+  const rsrc_t rs = DENSE ? make_rsrc(nullptr, 0)
+                          : make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * srb,
+                                      (int64_t)rows_n * srb);
   const rsrc_t rb = make_rsrc(biases ? biases + (int64_t)n_base * (K / 64) : nullptr,
                               biases ? (int64_t)rows_n * srb : 0);
   const int srow = wave * SROWS + lane;  // the tile row whose scales this lane loads
@@ -287,6 +304,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     for (int s = 0; s < WROWS / 8; ++s)
       buffer_load_lds16(ra, sb + (wave * WROWS + s * 8) * 8, a_off[s], k0 * 2);
     uint4* bc = sb + A_U4;
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int s = 0; s < BROWS / 8; ++s)
+        buffer_load_lds16(rc, bc + (wave * BROWS + s * 8) * 8, b_off[s], k0 * 2);
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < BC_LOADS; ++c) {
       const int p0 = wave * PPW + c * 64;
@@ -303,7 +326,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     }
   };
   // vector-memory loads one step issues per wave
-  constexpr int kStepLoads = WROWS / 8 + BC_LOADS + ((DEC == DEC_AFFINE) ? 2 : 1);
+  constexpr int kStepLoads =
+      WROWS / 8 + (DENSE ? BROWS / 8 : BC_LOADS + ((DEC == DEC_AFFINE) ? 2 : 1));
 
   // this lane's weight rows within the tile
   int nl[WNT];
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     load_step(min(st + 2, nsteps - 1), stage(pi));
     const uint4* cur = stage(si);
     BFrag b[WNT];
-    read_b(cur, st, b);
+    if constexpr (!DENSE) read_b(cur, st, b);
     // A fragments of sub-step kk + 1 are read while kk's MFMAs run
     auto read_a = [&](int kk, uint4 (&a)[WMT]) {
 #pragma unroll
@@ -362,7 +386,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     auto mma = [&](int kk, const uint4 (&a)[WMT]) {
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        const Op8 bo = expand<DEC>(b[j], kk);
+        Op8 bo;
+        if constexpr (DENSE) {
+          const uint4 v = cur[A_U4 + nl[j] * 8 + swz(nl[j], 4 * h + kk)];
+          bo.v[0] = v.x, bo.v[1] = v.y, bo.v[2] = v.z, bo.v[3] = v.w;
+        } else {
+          bo = expand<DEC>(b[j], kk);
+        }
 #pragma unroll
         for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], bo, acc[i][j]);
       }
@@ -442,6 +472,20 @@ hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* 
                   const float* g2, uint16_t* y, hipStream_t s) {
   const LaunchEvents ev = take_launch_events();
   launch_dq<DEC, WGM, WGN, WMT, WNT>(A, M, w, 0, (int)w.rows, g1, g2, y, s, ev.start, ev.stop);
+  return hipGetLastError();
+}
+
+// Dense bf16 GEMM y[M, N] = x . B^T on the same kernel (B bf16 [N, K]):
+// 256 x 128 tiles on 8 waves (128 x 32 per wave), three 48 KB LDS stages.
+hipError_t run_dense(const uint16_t* A, int M, const uint16_t* B, int N, int K, uint16_t* y,
+                     hipStream_t s) {
+  constexpr int WGM = 2, WGN = 4, WMT = 4, WNT = 1;
+  constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  launch_main(&gemm_dq_kernel<DEC_DENSE, WGM, WGN, WMT, WNT>, dim3(tiles_m * tiles_n),
+              dim3(64 * WGM * WGN), 0u, s, A, reinterpret_cast<const uint32_t*>(B),
+              (const void*)nullptr, (const uint16_t*)nullptr, (const float*)nullptr,
+              (const float*)nullptr, M, N, K, y, N, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -808,6 +852,18 @@ size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act) {
     return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
   }
   return 0;
+}
+
+// Dense prefill path: W dequantized to bf16 (global scale included) into the
+// caller's scratch, then the dense bf16 GEMM.
+hipError_t launch_qmm_dense(const uint16_t* x, int64_t M, const bsfp_qtensor& w, void* scratch,
+                            uint16_t* y, hipStream_t s) {
+  // (a pending bsfp_time_next_launch pair stays for the GEMM: the dequantize
+  // kernel launches without it)
+  uint16_t* wd = reinterpret_cast<uint16_t*>(scratch);
+  const hipError_t e = launch_dequantize(w, wd, s);
+  if (e != hipSuccess) return e;
+  return run_dense(x, (int)M, wd, (int)w.rows, (int)w.cols, y, s);
 }
 
 hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int act, void* ws,

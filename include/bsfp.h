@@ -154,7 +154,9 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
  * K = w->cols, x bf16 [M, K] row-major, W in the "transposed" MLX layout
  * [N, K] (QQMatmul::eval_gpu, w_transposed = true, lda = ldb = K:
  * "mlx 0.30.7.3 -> 0.30.7.6", qqmm.cpp).
- *   act == BSFP_ACT_BF16: y = x . dq(W)^T (bf16 MFMA, W dequantized in LDS).
+ *   act == BSFP_ACT_BF16: y = x . dq(W)^T (bf16 MFMA; W's codes are staged
+ *     in LDS and dequantized in registers, the global scale of NVFP4 applied
+ *     to the fp32 sums).
  *   act == BSFP_ACT_SAME: x is quantized into `workspace` with W's mode
  *     (quantize_input in the same file), then y = alpha * dq0(q(x)) .
  *     dq0(W)^T, dq0 = dequantization without the global scale, alpha =
@@ -165,7 +167,8 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
  *     MFMA with both operands dequantized exactly.  For M <= 8 (decode) the
  *     same product runs as the GEMV of bsfp_qmv on q(x) dequantized exactly
  *     to bf16, with alpha applied the same way (the M = 1 branch of
- *     QQMatmul, qqmm.cpp, with the global scale of w kept).
+ *     QQMatmul, qqmm.cpp, with the global scale of w kept); when x is at
+ *     most 64 KB the GEMV quantizes x itself, in one launch.
  * fp32 accumulation, bf16 (RNE) output.  `workspace` must hold
  * bsfp_qmm_workspace_bytes(...) bytes (16-byte aligned) and is overwritten.
  * x and y must be 16-byte aligned, w's scales and biases 4-byte aligned.
@@ -179,9 +182,37 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
                      uint16_t* y, bsfp_stream stream);
 
 /*
+ * bsfp_qmm_dense_scratch_bytes: bytes of the bf16 copy of a [rows, cols]
+ * weight that bsfp_qmm_dense dequantizes into (rows * cols * 2); 0 for
+ * negative arguments.
+ */
+size_t bsfp_qmm_dense_scratch_bytes(int64_t rows, int64_t cols);
+
+/*
+ * bsfp_qmm_dense: the dense prefill path of "mlx: opt-in dense GEMM for
+ * nvfp4 prefill (dequantise to bf16 above a row threshold)": W is
+ * dequantized to bf16 exactly as bsfp_dequantize does (NVFP4 with its global
+ * scale, rounded once to bf16) into `scratch`, then y = x . scratch^T with
+ * a dense bf16 GEMM (bf16 MFMA, fp32 accumulation, bf16 RNE output).  x bf16
+ * [M, K], y bf16 [M, N], N = w->rows, K = w->cols, every mode.
+ * `scratch` is caller-owned device memory of at least
+ * bsfp_qmm_dense_scratch_bytes(N, K) bytes, 16-byte aligned, not
+ * overlapping x or y; it is overwritten and may be reused for the next
+ * layer once the call's stream has passed it, so the transient is bounded
+ * by one layer's bf16 copy.  Picking this path above a row threshold is the
+ * caller's policy (the binding's qmm(dense_rows=...)).  Same limits and
+ * alignment rules as bsfp_qmm with BSFP_ACT_BF16; outside them the call
+ * returns BSFP_ERR_UNSUPPORTED (or BSFP_ERR_ARG for bad pointers or a small
+ * scratch) and launches nothing.
+ */
+bsfp_status bsfp_qmm_dense(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
+                           void* scratch, size_t scratch_bytes, uint16_t* y,
+                           bsfp_stream stream);
+
+/*
  * bsfp_time_next_launch: measurement hook.  The main kernel of this
- * thread's next bsfp_qmv or bsfp_qmm call (the GEMV, or the GEMM of
- * bsfp_qmm) is launched with hipExtLaunchKernelGGL, whose start and stop
+ * thread's next bsfp_qmv, bsfp_qmm or bsfp_qmm_dense call (the GEMV, or the
+ * GEMM) is launched with hipExtLaunchKernelGGL, whose start and stop
  * events then carry that kernel's own begin and end times, with no extra
  * commands queued between kernels.  start_event and stop_event are hipEvent_t
  * handles the caller created (timing enabled) and still owns; either may be

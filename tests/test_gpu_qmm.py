@@ -254,3 +254,93 @@ def test_qmm_unsupported_cases(bsfp):
     with pytest.raises(bsfp.BsfpError) as ei:
         bsfp.qmm(x, qa, act="same")
     assert ei.value.status == 2
+
+
+# ---------------------------------------------------------------- dense path
+# W dequantized to bf16 into a caller-owned scratch, then a dense bf16 GEMM
+# ("mlx: opt-in dense GEMM for nvfp4 prefill").  Against the oracle's dense
+# reference the operands are identical and exact, so only fp32 summation
+# order and the output rounding remain: the qq bar.
+
+def check_dense(o, b, x, qo, scratch=None, tol=QQ_TOL):
+    qd = oracle_to_dev(b, o, qo)
+    y = from_dev(b.qmm_dense(to_dev(x), qd, scratch=scratch))
+    yref, den = o.matmul_dense(x, qo)
+    e = o.norm_err(y, yref, den)
+    assert e.max() <= tol, (e.max(), np.unravel_index(e.argmax(), e.shape))
+    return y
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_dense_ragged(oracle_mod, bsfp, mode, M, N, K):
+    x = S.generic((M, K), 1.0, seed=1500 + M, stream=K)
+    w = S.generic((N, K), 0.02, seed=1501 + mode, stream=N)
+    check_dense(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+def test_dense_scratch_reused_across_layers(oracle_mod, bsfp):
+    """One scratch buffer serves two layers in a row (the bounded transient):
+    each result is that layer's product."""
+    o = oracle_mod
+    N, K = 700, 1024
+    scratch = torch.empty(bsfp.qmm_dense_scratch_bytes(N, K), dtype=torch.uint8, device="cuda")
+    for layer in range(2):
+        x = S.generic((300, K), 1.0, seed=1600 + layer)
+        w = S.generic((N, K), 0.02, seed=1610 + layer)
+        check_dense(o, bsfp, x, o.quantize(2, w), scratch=scratch)
+
+
+def test_dense_policy_by_rows(oracle_mod, bsfp):
+    """qmm(dense_rows=R): calls of at least R rows take the dense path (bit
+    for bit the qmm_dense result), smaller ones the fused kernel."""
+    o = oracle_mod
+    w = S.generic((400, 512), 0.02, seed=1620)
+    qd = oracle_to_dev(bsfp, o, o.quantize(2, w))
+    big = to_dev(S.generic((64, 512), 1.0, seed=1621))
+    small = to_dev(S.generic((16, 512), 1.0, seed=1622))
+    assert torch.equal(bsfp.qmm(big, qd, dense_rows=64), bsfp.qmm_dense(big, qd))
+    assert torch.equal(bsfp.qmm(small, qd, dense_rows=64), bsfp.qmm(small, qd))
+
+
+def test_dense_errors(bsfp):
+    x = to_dev(S.generic((4, 128), 1.0, seed=1))
+    q = bsfp.quantize(to_dev(S.generic((8, 128), 1.0, seed=2)), 2)
+    small = torch.empty(8 * 128 * 2 - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsfp.BsfpError) as ei:
+        bsfp.qmm_dense(x, q, scratch=small)
+    assert ei.value.status == 1
+    x96 = to_dev(S.generic((4, 96), 1.0, seed=1))
+    q96 = bsfp.quantize(to_dev(S.generic((8, 96), 1.0, seed=2)), 2)
+    with pytest.raises(bsfp.BsfpError) as ei:
+        bsfp.qmm_dense(x96, q96)
+    assert ei.value.status == 2
+
+
+def test_dense_deterministic(bsfp):
+    x = to_dev(S.generic((300, 1024), 1.0, seed=3))
+    q = bsfp.quantize(to_dev(S.generic((700, 1024), 0.02, seed=4)), 2)
+    assert torch.equal(bsfp.qmm_dense(x, q), bsfp.qmm_dense(x, q))
+
+
+@pytest.mark.parametrize("M", [1134, 2048])
+def test_dense_prefill_sampled_full_size(oracle_mod, bsfp, M):
+    """X[M,5120] . W[25600,5120]^T (NVFP4, global scale) at full size: 8 full
+    output rows plus 2048 random outputs against the oracle's dense
+    reference, computed one by one."""
+    o = oracle_mod
+    x, w = S.nvfp4_prefill(M=M, N=25600, K=5120, seed=7)
+    qo = o.quantize(2, w)
+    qd = oracle_to_dev(bsfp, o, qo)
+    y = from_dev(bsfp.qmm_dense(to_dev(x), qd))
+    rng = np.random.default_rng(7)
+    rows = rng.choice(M, 8, replace=False)
+    ai = np.concatenate([np.repeat(rows, 25600), rng.integers(0, M, 2048)])
+    bi = np.concatenate([np.tile(np.arange(25600), 8), rng.integers(0, 25600, 2048)])
+    ua, ia = np.unique(ai, return_inverse=True)
+    ub, ib = np.unique(bi, return_inverse=True)
+    A = o.bf16_to_f64(x[ua])
+    B = o.matmul_dense(None, qo, rows=ub)
+    yref, den = o.matmul_pairs(A, B, ia, ib)
+    e = o.norm_err(y[ai, bi], yref, den)
+    assert e.max() <= QQ_TOL, e.max()
