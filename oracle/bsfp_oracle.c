@@ -30,6 +30,13 @@
  *   R7  packing: low nibble first, 8 codes per little-endian uint32.
  *   R8  dequant: NVFP4 bf16((E2M1*E4M3)*g); MXFP4 bf16(E2M1*2^e); affine
  *       bf16(fma(sb, q, bb)).
+ *   R9  stochastic rounding (the USE_SR variant of the 4-bit quantizer; the
+ *       pages give no rounding rule or random-bit contract): scales as in
+ *       R4/R5; an element |v| strictly between grid magnitudes lo < hi
+ *       becomes hi when u < p, else lo, with p = (|v| - lo) / (hi - lo) and
+ *       u = (r >> 8) * 2^-24 for the element's caller-supplied 32-bit r;
+ *       both are exact in fp32.  Grid values stay, |v| >= 6 saturates, the
+ *       sign bit follows v.  E[E2M1(v)] = v up to 2^-24 of the spacing.
  *
  * Parity status: the codecs, packing, the exact-reproduction cases, the
  * invariants and the matmul are pinned by the not-gpu test suite (closed
@@ -136,6 +143,23 @@ int bo_e2m1_encode(float v)
      * 7 (for very large |v| the fp64 distances to 4 and 6 would tie). */
     if (a >= 6.0) best = 7;
     return best | (signbit(v) ? 8 : 0);
+}
+
+/* [R9] Stochastic rounding to E2M1 with the random word r. */
+int bo_e2m1_encode_sr(float v, uint32_t r)
+{
+    const int sign = signbit(v) ? 8 : 0;
+    const float a = fabsf(v);
+    if (!(a < 6.0f)) return 7 | sign; /* saturate (NaN too) */
+    int lo = 0; /* largest grid magnitude <= a */
+    for (int c = 1; c < 8; ++c)
+        if (bo_e2m1_decode(c) <= (double)a) lo = c;
+    const float flo = (float)bo_e2m1_decode(lo);
+    if (flo == a) return lo | sign;
+    const float fhi = (float)bo_e2m1_decode(lo + 1);
+    const float p = (a - flo) / (fhi - flo); /* exact: Sterbenz, power-of-two divisor */
+    const float u = (float)(r >> 8) * 0x1p-24f;
+    return (u < p ? lo + 1 : lo) | sign;
 }
 
 void bo_e2m1_encode_array(const float* v, int64_t n, uint8_t* out)
@@ -245,10 +269,10 @@ static int get_code(const uint32_t* row_words, int64_t k)
  * NVFP4/MXFP4 conversion on Blackwell builds", Current Behavior: the
  * scale-then-convert helpers; "mlx 0.30.7.3 -> 0.30.7.6", quantized.h,
  * fp_quantize with a global scale). */
-void bo_quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
-                       int use_global, const float* g_given,
-                       uint32_t* codes, uint8_t* scales,
-                       float* g_out, float* amax_out)
+static void quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
+                           int use_global, const float* g_given,
+                           uint32_t* codes, uint8_t* scales,
+                           float* g_out, float* amax_out, const uint32_t* rbits)
 {
     const int G = 16;
     float g = 1.0f;
@@ -289,10 +313,29 @@ void bo_quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
             float inv = 1.0f / d;
             for (int i = 0; i < G; ++i) {
                 float v = bo_bf16_to_f32(xr[b * G + i]) * inv;
-                put_code(cr, b * G + i, bo_e2m1_encode(v));
+                int c = rbits ? bo_e2m1_encode_sr(v, rbits[r * cols + b * G + i])
+                              : bo_e2m1_encode(v);
+                put_code(cr, b * G + i, c);
             }
         }
     }
+}
+
+void bo_quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
+                       int use_global, const float* g_given,
+                       uint32_t* codes, uint8_t* scales,
+                       float* g_out, float* amax_out)
+{
+    quantize_nvfp4(x, rows, cols, use_global, g_given, codes, scales, g_out, amax_out, NULL);
+}
+
+/* [R9] NVFP4 with stochastically rounded codes; rbits [rows, cols]. */
+void bo_quantize_nvfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
+                          int use_global, const float* g_given, const uint32_t* rbits,
+                          uint32_t* codes, uint8_t* scales,
+                          float* g_out, float* amax_out)
+{
+    quantize_nvfp4(x, rows, cols, use_global, g_given, codes, scales, g_out, amax_out, rbits);
 }
 
 /* ======================================================================== */
@@ -312,8 +355,8 @@ static int floor_log2(double a)
  * amax, elements scaled exactly by 2^-e and converted to E2M1 (the MX arm of
  * the same bits == 4 quantizer, "perf(cuda): enable hardware NVFP4/MXFP4
  * conversion on Blackwell builds", Current Behavior, use_mx_scale). */
-void bo_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
-                       uint32_t* codes, uint8_t* scales)
+static void quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
+                           uint32_t* codes, uint8_t* scales, const uint32_t* rbits)
 {
     const int G = 32;
     const int emax_e2m1 = 2; /* largest E2M1 magnitude 6 = 1.5 * 2^2 */
@@ -334,10 +377,25 @@ void bo_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
             scales[r * groups + b] = (uint8_t)(e + 127);
             for (int i = 0; i < G; ++i) {
                 float v = ldexpf(bo_bf16_to_f32(xr[b * G + i]), -e);
-                put_code(cr, b * G + i, bo_e2m1_encode(v));
+                int c = rbits ? bo_e2m1_encode_sr(v, rbits[r * cols + b * G + i])
+                              : bo_e2m1_encode(v);
+                put_code(cr, b * G + i, c);
             }
         }
     }
+}
+
+void bo_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
+                       uint32_t* codes, uint8_t* scales)
+{
+    quantize_mxfp4(x, rows, cols, codes, scales, NULL);
+}
+
+/* [R9] MXFP4 with stochastically rounded codes; rbits [rows, cols]. */
+void bo_quantize_mxfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
+                          const uint32_t* rbits, uint32_t* codes, uint8_t* scales)
+{
+    quantize_mxfp4(x, rows, cols, codes, scales, rbits);
 }
 
 /* ======================================================================== */

@@ -28,6 +28,7 @@ uint16_t bo_bf16_from_f32(float f);
 uint16_t bo_bf16_from_f64(double d);
 double   bo_e2m1_decode(int code);
 int      bo_e2m1_encode(float v);
+int      bo_e2m1_encode_sr(float v, uint32_t r);
 double   bo_e4m3_decode(int code);
 int      bo_e4m3_encode(float s); /* s >= 0 */
 double   bo_e8m0_decode(int code);
@@ -55,6 +56,12 @@ void bo_quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
 /* MXFP4, group 32, E8M0 scales. */
 void bo_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
                        uint32_t* codes, uint8_t* scales);
+void bo_quantize_nvfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
+                          int use_global, const float* g_given, const uint32_t* rbits,
+                          uint32_t* codes, uint8_t* scales,
+                          float* g_out, float* amax_out);
+void bo_quantize_mxfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
+                          const uint32_t* rbits, uint32_t* codes, uint8_t* scales);
 /* Affine 4-bit, group 64, bf16 scale and bias. */
 void bo_quantize_affine(const uint16_t* x, int64_t rows, int64_t cols,
                         uint32_t* codes, uint16_t* scales, uint16_t* biases);

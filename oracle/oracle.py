@@ -61,6 +61,9 @@ def lib():
             "bo_alpha": (C.c_float, [C.c_float, C.c_float]),
             "bo_quantize_nvfp4": (None, [_P, _I64, _I64, C.c_int, _P, _P, _P, _P, _P]),
             "bo_quantize_mxfp4": (None, [_P, _I64, _I64, _P, _P]),
+            "bo_quantize_nvfp4_sr": (None, [_P, _I64, _I64, C.c_int, _P, _P, _P, _P, _P, _P]),
+            "bo_quantize_mxfp4_sr": (None, [_P, _I64, _I64, _P, _P, _P]),
+            "bo_e2m1_encode_sr": (C.c_int, [C.c_float, C.c_uint32]),
             "bo_quantize_affine": (None, [_P, _I64, _I64, _P, _P, _P]),
             "bo_dequantize_nvfp4": (None, [_P, _P, _P, _I64, _I64, _P]),
             "bo_dequantize_mxfp4": (None, [_P, _P, _I64, _I64, _P]),
@@ -126,6 +129,11 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
     return out
 
 
+def e2m1_encode_sr(v: float, r: int) -> int:
+    """Stochastic rounding of one fp32 value to an E2M1 code (reading R9)."""
+    return int(lib().bo_e2m1_encode_sr(float(np.float32(v)), int(r) & 0xFFFFFFFF))
+
+
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     out = np.empty(v.shape, np.uint8)
@@ -163,9 +171,11 @@ class QTensor:
 
 
 def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
-             g: Optional[float] = None) -> QTensor:
+             g: Optional[float] = None, rbits: Optional[np.ndarray] = None) -> QTensor:
     """Quantize a bf16 [rows, cols] tensor.  For NVFP4, use_global selects a
-    per-tensor global scale, either the given g or amax/2688 computed here."""
+    per-tensor global scale, either the given g or amax/2688 computed here.
+    rbits (uint32 [rows, cols], NVFP4 / MXFP4 only) selects stochastic
+    rounding of the codes with those random words (reading R9)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x_bits.ndim == 1:
         x_bits = x_bits.reshape(1, -1)
@@ -173,6 +183,10 @@ def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
     G = GROUP[mode]
     if cols % G:
         raise ValueError(f"cols={cols} is not a multiple of the group size {G}")
+    if rbits is not None:
+        if mode == AFFINE:
+            raise ValueError("stochastic rounding applies to NVFP4 and MXFP4")
+        rbits = np.ascontiguousarray(rbits, dtype=np.uint32).reshape(rows, cols)
     codes = np.zeros((rows, cols // 8), np.uint32)
     L = lib()
     if mode == NVFP4:
@@ -180,14 +194,23 @@ def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
         g_out = np.zeros(1, np.float32)
         amax_out = np.full(1, np.nan, np.float32)
         g_in = None if g is None else np.array([g], np.float32)
-        L.bo_quantize_nvfp4(_ptr(x_bits), rows, cols, int(bool(use_global)), _ptr(g_in),
-                            _ptr(codes), _ptr(scales), _ptr(g_out), _ptr(amax_out))
+        if rbits is None:
+            L.bo_quantize_nvfp4(_ptr(x_bits), rows, cols, int(bool(use_global)), _ptr(g_in),
+                                _ptr(codes), _ptr(scales), _ptr(g_out), _ptr(amax_out))
+        else:
+            L.bo_quantize_nvfp4_sr(_ptr(x_bits), rows, cols, int(bool(use_global)), _ptr(g_in),
+                                   _ptr(rbits), _ptr(codes), _ptr(scales), _ptr(g_out),
+                                   _ptr(amax_out))
         return QTensor(mode, rows, cols, codes, scales, None,
                        np.float32(g_out[0]) if use_global else None,
                        None if np.isnan(amax_out[0]) else np.float32(amax_out[0]))
     if mode == MXFP4:
         scales = np.zeros((rows, cols // G), np.uint8)
-        L.bo_quantize_mxfp4(_ptr(x_bits), rows, cols, _ptr(codes), _ptr(scales))
+        if rbits is None:
+            L.bo_quantize_mxfp4(_ptr(x_bits), rows, cols, _ptr(codes), _ptr(scales))
+        else:
+            L.bo_quantize_mxfp4_sr(_ptr(x_bits), rows, cols, _ptr(rbits), _ptr(codes),
+                                   _ptr(scales))
         return QTensor(mode, rows, cols, codes, scales)
     if mode == AFFINE:
         scales = np.zeros((rows, cols // G), np.uint16)

@@ -90,6 +90,13 @@ def generic(shape, std: float = 1.0, seed: int = 0, stream: int = 0):
     return normal_bf16(rng_for(seed, stream), shape, std)
 
 
+def random_words(shape, seed: int = 0, stream: int = 0) -> np.ndarray:
+    """Uniform random uint32 words: the random input of stochastic-rounding
+    quantize (one word per element), passed to both the kernel and the
+    oracle."""
+    return rng_for(seed, 1000 + stream).integers(0, 1 << 32, size=shape, dtype=np.uint32)
+
+
 def torch_normal_bf16(shape, std: float, seed: int, device) -> torch.Tensor:
     """Device-side draw (torch's Philox generator) for large benchmark sweeps
     whose numbers never meet the oracle; returns a bf16 tensor on `device`."""
