@@ -8,6 +8,8 @@ already resident in HBM:
               E4M3 scales + global scale), 1 % outliers at +-20
   dequant     NVFP4 dequantize of the same tensor
   w_quant     MXFP4 quantize W[5760,2880] and affine quantize W[1024,512]
+  act_quant_sr  NVFP4 quantize of the same X with stochastic rounding (one
+              random word per element, drawn on the device beforehand)
   qmv_sweep   affine g64 decode GEMV over 64 layers x {gate, up, down}
               ([25600,5120], [25600,5120], [5120,25600]): 192 distinct matrices,
               14.17 GB of packed weights (more than the 256 MB Infinity Cache)
@@ -149,6 +151,13 @@ def main():
     def st_act_quant():
         b.quantize(X_act, b.NVFP4, "compute", out=q_act)
 
+    rbits_act = torch.randint(-(1 << 31), (1 << 31) - 1, (4096 * HIDDEN,), dtype=torch.int32,
+                              device=dev)
+    q_act_sr = b.empty_quantized(b.NVFP4, 4096, HIDDEN, dev)
+
+    def st_act_quant_sr():
+        b.quantize(X_act, b.NVFP4, "compute", out=q_act_sr, rbits=rbits_act)
+
     def st_dequant():
         b.dequantize(q_act, out=dq_act)
 
@@ -203,7 +212,8 @@ def main():
     def dense(M):
         return lambda: b.qmm_dense(X_pf[M], q_pf, scratch=dense_scratch, out=Y_pf[M])
 
-    stages = [("act_quant", st_act_quant), ("dequant", st_dequant), ("w_quant", st_w_quant),
+    stages = [("act_quant", st_act_quant), ("act_quant_sr", st_act_quant_sr),
+              ("dequant", st_dequant), ("w_quant", st_w_quant),
               ("qmv_sweep", st_qmv_sweep), ("qmv_fp4", st_qmv_fp4), ("qqmm", qq(2048)),
               ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qq_decode", st_qq_decode),
               ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)),
@@ -323,6 +333,9 @@ def main():
     if "act_quant" in ms:
         nbytes = 4096 * HIDDEN * 2 * 2 + 4096 * HIDDEN // 2 + 4096 * HIDDEN // 16
         out["act_quant_gbs"] = round(nbytes / (ms["act_quant"] * 1e-3) / 1e9, 1)
+    if "act_quant_sr" in ms:  # + 4 bytes of random word per element
+        nbytes = 4096 * HIDDEN * (2 * 2 + 4) + 4096 * HIDDEN // 2 + 4096 * HIDDEN // 16
+        out["act_quant_sr_gbs"] = round(nbytes / (ms["act_quant_sr"] * 1e-3) / 1e9, 1)
 
     if not args.no_cpu_baseline and out["value"] is not None:
         out["cpu_baseline"] = cpu_baseline(log)

@@ -29,7 +29,8 @@ ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
 
 EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
-           "bsfp_qmm_workspace_bytes", "bsfp_qmm", "bsfp_qmm_dense_scratch_bytes",
+           "bsfp_quantize_sr", "bsfp_qmm_workspace_bytes", "bsfp_qmm",
+           "bsfp_qmm_dense_scratch_bytes",
            "bsfp_qmm_dense", "bsfp_time_next_launch", "bsfp_last_error", "bsfp_version")
 
 
@@ -63,6 +64,7 @@ def lib():
         sigs = {
             "bsfp_amax": (C.c_int, [P, I64, P, P]),
             "bsfp_quantize": (C.c_int, [P, QP, I32, P]),
+            "bsfp_quantize_sr": (C.c_int, [P, QP, I32, P, P]),
             "bsfp_dequantize": (C.c_int, [QP, P, P]),
             "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
             "bsfp_qmm_workspace_bytes": (C.c_size_t, [I32, I64, I64, I32]),
@@ -178,9 +180,12 @@ def amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
 
 def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
              g: Optional[torch.Tensor] = None,
-             out: Optional[QuantizedTensor] = None) -> QuantizedTensor:
+             out: Optional[QuantizedTensor] = None,
+             rbits: Optional[torch.Tensor] = None) -> QuantizedTensor:
     """Quantize a bf16 [rows, cols] GPU tensor.  For NVFP4, global_scale is
-    'compute' (g = amax/2688), 'given' (use the fp32 [1] tensor g) or 'none'."""
+    'compute' (g = amax/2688), 'given' (use the fp32 [1] tensor g) or 'none'.
+    rbits (uint32 words, one per element, NVFP4 / MXFP4): stochastic rounding
+    of the codes with those random words (bsfp_quantize_sr)."""
     x2 = _as_2d_bf16(x)
     rows, cols = x2.shape
     gs = {"none": GS_NONE, "compute": GS_COMPUTE, "given": GS_GIVEN}[global_scale]
@@ -193,6 +198,12 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
     if mode == NVFP4 and gs == GS_NONE:
         out.global_scale = None
     d = out.desc()
+    if rbits is not None:
+        if rbits.numel() != rows * cols or rbits.element_size() != 4 or not rbits.is_contiguous():
+            raise ValueError("rbits needs one contiguous 32-bit word per element")
+        _check(lib().bsfp_quantize_sr(_ptr(x2), C.byref(d), gs if mode == NVFP4 else 0,
+                                      _ptr(rbits), _stream()))
+        return out
     _check(lib().bsfp_quantize(_ptr(x2), C.byref(d), gs if mode == NVFP4 else 0, _stream()))
     return out
 

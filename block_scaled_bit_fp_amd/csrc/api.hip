@@ -150,22 +150,23 @@ bsfp_status bsfp_amax(const uint16_t* x, int64_t n, float* amax_out, bsfp_stream
   return device_status(launch_amax(x, n, amax_out, (hipStream_t)stream), "bsfp_amax");
 }
 
-bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
-                          bsfp_stream stream) {
-  bsfp_status st = check_qtensor(q, "bsfp_quantize");
+// bsfp_quantize and bsfp_quantize_sr (rbits != nullptr: stochastic rounding).
+static bsfp_status quantize_impl(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                          const uint32_t* rbits, bsfp_stream stream, const char* fn) {
+  bsfp_status st = check_qtensor(q, fn);
   if (st != BSFP_OK) return st;
   const int64_t n = q->rows * q->cols;
   hipStream_t s = (hipStream_t)stream;
   if (q->mode == BSFP_NVFP4) {
     if (gs < BSFP_GS_NONE || gs > BSFP_GS_GIVEN)
-      return fail(BSFP_ERR_ARG, "bsfp_quantize: bad global-scale flag %d", (int)gs);
+      return fail(BSFP_ERR_ARG, "%s: bad global-scale flag %d", fn, (int)gs);
     if (gs != BSFP_GS_NONE && !q->global_scale)
-      return fail(BSFP_ERR_ARG, "bsfp_quantize: nvfp4 global scale requested but global_scale is null");
+      return fail(BSFP_ERR_ARG, "%s: nvfp4 global scale requested but global_scale is null", fn);
     if (gs == BSFP_GS_COMPUTE && !q->amax)
-      return fail(BSFP_ERR_ARG, "bsfp_quantize: BSFP_GS_COMPUTE needs an amax buffer");
+      return fail(BSFP_ERR_ARG, "%s: BSFP_GS_COMPUTE needs an amax buffer", fn);
   }
   if (n > 0 && (!x || !aligned16(x)))
-    return fail(BSFP_ERR_ARG, "bsfp_quantize: x is null or not 16-byte aligned");
+    return fail(BSFP_ERR_ARG, "%s: x is null or not 16-byte aligned", fn);
   const int64_t n_words = n / 8;
   hipError_t e = hipSuccess;
   switch (q->mode) {
@@ -174,21 +175,38 @@ bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
         e = launch_amax(x, n, q->amax, s);
         if (e == hipSuccess)
           e = launch_quantize_nvfp4(x, n_words, q->codes, (uint8_t*)q->scales, q->amax, 1,
-                                    q->global_scale, s);
+                                    q->global_scale, s, rbits);
       } else if (n_words > 0) {
         e = launch_quantize_nvfp4(x, n_words, q->codes, (uint8_t*)q->scales,
-                                  gs == BSFP_GS_GIVEN ? q->global_scale : nullptr, 0, nullptr, s);
+                                  gs == BSFP_GS_GIVEN ? q->global_scale : nullptr, 0, nullptr, s,
+                                  rbits);
       }
       break;
     case BSFP_MXFP4:
-      if (n_words > 0) e = launch_quantize_mxfp4(x, n_words, q->codes, (uint8_t*)q->scales, s);
+      if (n_words > 0)
+        e = launch_quantize_mxfp4(x, n_words, q->codes, (uint8_t*)q->scales, s, rbits);
       break;
     default:
       if (n_words > 0)
         e = launch_quantize_affine(x, n_words, q->codes, (uint16_t*)q->scales, q->biases, s);
       break;
   }
-  return device_status(e, "bsfp_quantize");
+  return device_status(e, fn);
+}
+
+bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                          bsfp_stream stream) {
+  return quantize_impl(x, q, gs, nullptr, stream, "bsfp_quantize");
+}
+
+bsfp_status bsfp_quantize_sr(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                             const uint32_t* rbits, bsfp_stream stream) {
+  if (q && q->mode != BSFP_NVFP4 && q->mode != BSFP_MXFP4)
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_quantize_sr: stochastic rounding applies to nvfp4 and mxfp4 only");
+  if (q && q->rows * q->cols > 0 && (!rbits || !aligned16(rbits)))
+    return fail(BSFP_ERR_ARG, "bsfp_quantize_sr: rbits is null or not 16-byte aligned");
+  return quantize_impl(x, q, gs, rbits, stream, "bsfp_quantize_sr");
 }
 
 bsfp_status bsfp_dequantize(const bsfp_qtensor* q, uint16_t* out, bsfp_stream stream) {

@@ -82,6 +82,46 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
   return w;
 }
 
+// Stochastic rounding of v to an E2M1 code with the random word r: between
+// grid magnitudes lo < hi, hi when (r >> 8) * 2^-24 < (|v| - lo) / (hi - lo)
+// (both exact in fp32), else lo; grid values stay, |v| >= 6 (or NaN)
+// saturates, the sign bit follows v.
+__device__ __forceinline__ uint32_t e2m1_encode_sr(float v, uint32_t r) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 3;
+  const float a = fabsf(v);
+  if (!(a < 6.0f)) return 7u | sign;
+  uint32_t lo;
+  float flo, inv_step;
+  if (a < 2.0f) {  // grid 0, 0.5, 1, 1.5: code = floor(2a)
+    lo = (uint32_t)(a * 2.0f);
+    flo = (float)lo * 0.5f;
+    inv_step = 2.0f;
+  } else if (a < 4.0f) {  // grid 2, 3: codes 4, 5
+    const uint32_t t = (uint32_t)a;
+    lo = t + 2u;
+    flo = (float)t;
+    inv_step = 1.0f;
+  } else {  // grid 4 (code 6), next 6
+    lo = 6u;
+    flo = 4.0f;
+    inv_step = 0.5f;
+  }
+  const float p = (a - flo) * inv_step;  // exact: Sterbenz, power-of-two step
+  const float u = (float)(r >> 8) * 5.9604644775390625e-08f;  // 2^-24, exact
+  return (lo + (u < p ? 1u : 0u)) | sign;
+}
+
+// Eight fp32 -> one packed word with stochastic rounding; word i of (r0, r1)
+// (r0.x .. r1.w) belongs to element i.
+__device__ __forceinline__ uint32_t e2m1_pack8_sr(const float (&v)[8], const uint4& r0,
+                                                  const uint4& r1) {
+  const uint32_t r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_encode_sr(v[i], r[i]) << (4 * i);
+  return w;
+}
+
 // Byte `SEL` of w (two codes) -> two bf16 values (low nibble -> .x), exact.
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {

@@ -39,9 +39,11 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_
 // NVFP4 quantize.  g_src: NULL (no global scale, g = 1), or a device fp32
 // holding g (g_src_is_amax == 0) or the tensor amax (g_src_is_amax == 1, g =
 // amax/2688).  g_out (may be NULL) receives the g used.
+// rbits: stochastic rounding with 8 random words per packed word (element
+// order), or nullptr for round-to-nearest.
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, const float* g_src, int g_src_is_amax,
-                                 float* g_out, hipStream_t s);
+                                 float* g_out, hipStream_t s, const uint32_t* rbits = nullptr);
 // NVFP4 quantize + dequantize without the global scale into fp16 xhat
 // [n_words * 8] (the qq GEMM's activation operand).
 hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words, void* xhat,
@@ -55,7 +57,7 @@ hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words
 hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
                                               hipStream_t s);
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
-                                 uint8_t* scales, hipStream_t s);
+                                 uint8_t* scales, hipStream_t s, const uint32_t* rbits = nullptr);
 hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                   uint16_t* scales, uint16_t* biases, hipStream_t s);
 

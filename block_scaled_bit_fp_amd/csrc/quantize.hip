@@ -81,10 +81,12 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------------ NVFP4
 
+// rbits (stochastic rounding, NULL for nearest): 8 random words per packed
+// word, element order.
 __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ g_src, int g_src_is_amax,
-    float* __restrict__ g_out) {
+    float* __restrict__ g_out, const uint4* __restrict__ rbits) {
   float g = 1.0f;
   if (g_src) g = g_src_is_amax ? (*g_src / 2688.0f) : *g_src;
   if (g_out && blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = f[k] * inv;
-      w = e2m1_pack8(v);
+      w = rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v);
     } else {
       S = 0;
     }
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
 
 __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, const uint4* __restrict__ rbits) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
     float f[8];
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
-    codes[i] = e2m1_pack8(v);
+    codes[i] = rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v);
     if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
   }
 }
@@ -308,10 +310,10 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_
 
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, const float* g_src, int g_src_is_amax,
-                                 float* g_out, hipStream_t s) {
+                                 float* g_out, hipStream_t s, const uint32_t* rbits) {
   hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
                      reinterpret_cast<const uint4*>(x), n_words, codes, scales, g_src,
-                     g_src_is_amax, g_out);
+                     g_src_is_amax, g_out, reinterpret_cast<const uint4*>(rbits));
   return hipGetLastError();
 }
 
@@ -342,9 +344,10 @@ hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words
 }
 
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
-                                 uint8_t* scales, hipStream_t s) {
+                                 uint8_t* scales, hipStream_t s, const uint32_t* rbits) {
   hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint4*>(x), n_words, codes, scales);
+                     reinterpret_cast<const uint4*>(x), n_words, codes, scales,
+                     reinterpret_cast<const uint4*>(rbits));
   return hipGetLastError();
 }
 

@@ -121,6 +121,24 @@ bsfp_status bsfp_quantize(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
                           bsfp_stream stream);
 
 /*
+ * bsfp_quantize_sr: bsfp_quantize with stochastic rounding of the E2M1
+ * codes, for NVFP4 and MXFP4 (the USE_SR variant of the 4-bit quantizer,
+ * "perf(cuda): enable hardware NVFP4/MXFP4 conversion on Blackwell builds",
+ * Current Behavior).  Scales, global scale and amax are exactly those of
+ * bsfp_quantize.  Element k (row-major over [rows, cols]) takes the random
+ * word rbits[k]: with its scaled value v between E2M1 grid magnitudes
+ * lo < hi, the code is hi when (rbits[k] >> 8) * 2^-24 < (|v| - lo) /
+ * (hi - lo), else lo (both sides exact in fp32); grid values stay, |v| >= 6
+ * saturates, the sign bit follows v.  The rounding is unbiased up to 2^-24
+ * of the grid spacing.  rbits: device pointer to q->rows * q->cols uint32,
+ * 16-byte aligned, owned by the caller, read only; the caller chooses how
+ * it is drawn.  AFFINE returns BSFP_ERR_UNSUPPORTED; other errors as for
+ * bsfp_quantize.
+ */
+bsfp_status bsfp_quantize_sr(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                             const uint32_t* rbits, bsfp_stream stream);
+
+/*
  * bsfp_dequantize: q -> bf16 out [q->rows, q->cols].  fp_dequantize /
  * affine_dequantize of "mlx 0.30.7.3 -> 0.30.7.6" (quantized.cpp).
  *   NVFP4  bf16((E2M1 * E4M3) * g)  (g = 1 when q->global_scale is NULL)

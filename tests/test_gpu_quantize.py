@@ -146,3 +146,91 @@ def test_quantize_is_deterministic(bsfp):
     a = bsfp.quantize(x, 2)
     b2 = bsfp.quantize(x, 2)
     assert torch.equal(a.codes, b2.codes) and torch.equal(a.scales, b2.scales)
+
+
+# ------------------------------------------------- stochastic rounding (SR)
+# The random words are inputs, drawn by the seeded input module and handed
+# to both sides, so codes and scales must be bit-exact.
+
+def check_sr_exact(o, b, x_bits, mode, r, gs="compute", g=None):
+    xd = to_dev(x_bits)
+    rd = torch.from_numpy(np.ascontiguousarray(r).view(np.int32)).to("cuda")
+    gd = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda")
+    q = b.quantize(xd, mode, global_scale=gs, g=gd, rbits=rd)
+    if mode == o.NVFP4:
+        qo = o.quantize(mode, x_bits, use_global=(gs != "none"), g=g, rbits=r)
+    else:
+        qo = o.quantize(mode, x_bits, rbits=r)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(q.codes), qo.codes), "codes differ"
+    assert np.array_equal(u8(q.scales), qo.scales), "scales differ"
+    if mode == o.NVFP4 and gs != "none":
+        assert q.global_scale.item() == qo.g
+    return q, qo
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("shape", [(1, 64), (37, 64 * 13), (3, 2880), (129, 5120)])
+def test_sr_ragged_shapes(oracle_mod, bsfp, mode, shape):
+    x = S.generic(shape, 1.5, seed=300 + mode, stream=shape[0])
+    r = S.random_words(shape, seed=301 + mode, stream=shape[0])
+    check_sr_exact(oracle_mod, bsfp, x, mode, r)
+
+
+def test_sr_nvfp4_global_scale_variants(oracle_mod, bsfp):
+    o = oracle_mod
+    x = S.generic((64, 1024), 0.02, seed=310)
+    r = S.random_words((64, 1024), seed=311)
+    check_sr_exact(o, bsfp, x, o.NVFP4, r, gs="given", g=3.7e-5)
+    check_sr_exact(o, bsfp, x, o.NVFP4, r, gs="none")
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_sr_every_bf16_value_and_extreme_words(oracle_mod, bsfp, mode):
+    """All finite bf16 values through the SR quantizer with random words, with
+    all-zero words (round up) and with all-one words (round down)."""
+    o = oracle_mod
+    x = _all_bf16_blocks()
+    gs = "none" if mode == 2 else "compute"
+    for r in (S.random_words(x.shape, seed=320 + mode),
+              np.zeros(x.shape, np.uint32), np.full(x.shape, 0xFFFFFFFF, np.uint32)):
+        check_sr_exact(o, bsfp, x, mode, r, gs=gs)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_sr_threshold_neighbourhoods(oracle_mod, bsfp, mode):
+    """Scaled values on, just below and just above every E2M1 grid value and
+    midpoint, with words near the decision u = p."""
+    o = oracle_mod
+    rng = np.random.default_rng(330 + mode)
+    pts = np.array([0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0])
+    rows = []
+    G = o.GROUP[mode]
+    for _ in range(64):
+        scale = float(2.0 ** rng.integers(-6, 6))
+        v = rng.choice(pts, G) * scale
+        v *= rng.choice([1 - 2 ** -7, 1.0, 1 + 2 ** -7], G)
+        v *= rng.choice([-1.0, 1.0], G)
+        v[0] = 6.0 * scale
+        rows.append(v)
+    x = S.to_bf16_bits(np.array(rows, np.float32).reshape(-1, 64))
+    r = (rng.integers(0, 1 << 24, x.shape, dtype=np.uint64) << 8).astype(np.uint32)
+    r[:, ::3] = 0x80000000  # u = 1/2 exactly: the midpoints decide on u < p
+    check_sr_exact(o, bsfp, x, mode, r, gs="none" if mode == 2 else "compute")
+
+
+def test_sr_nvfp4_activation_config(oracle_mod, bsfp):
+    """X[4096,5120] with 1 % outliers: SR codes bit-exact at full size."""
+    x = S.nvfp4_activations()
+    r = S.random_words(x.shape, seed=340)
+    check_sr_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4, r)
+
+
+def test_sr_rejects_affine_and_bad_words(bsfp):
+    x = to_dev(S.generic((4, 128), 1.0, seed=1))
+    r = torch.zeros(4 * 128, dtype=torch.int32, device="cuda")
+    with pytest.raises(bsfp.BsfpError) as ei:
+        bsfp.quantize(x, 0, rbits=r)
+    assert ei.value.status == 2
+    with pytest.raises(ValueError):
+        bsfp.quantize(x, 2, rbits=r[:100])
