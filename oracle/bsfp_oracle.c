@@ -30,7 +30,7 @@
  *   R7  packing: low nibble first, 8 codes per little-endian uint32.
  *   R8  dequant: NVFP4 bf16((E2M1*E4M3)*g); MXFP4 bf16(E2M1*2^e); affine
  *       bf16(fma(sb, q, bb)).
- *   R9  stochastic rounding (the USE_SR variant of the 4-bit quantizer; the
+ *   R15  stochastic rounding (the USE_SR variant of the 4-bit quantizer; the
  *       pages give no rounding rule or random-bit contract): scales as in
  *       R4/R5; an element |v| strictly between grid magnitudes lo < hi
  *       becomes hi when u < p, else lo, with p = (|v| - lo) / (hi - lo) and
@@ -145,7 +145,7 @@ int bo_e2m1_encode(float v)
     return best | (signbit(v) ? 8 : 0);
 }
 
-/* [R9] Stochastic rounding to E2M1 with the random word r. */
+/* [R15] Stochastic rounding to E2M1 with the random word r. */
 int bo_e2m1_encode_sr(float v, uint32_t r)
 {
     const int sign = signbit(v) ? 8 : 0;
@@ -329,7 +329,7 @@ void bo_quantize_nvfp4(const uint16_t* x, int64_t rows, int64_t cols,
     quantize_nvfp4(x, rows, cols, use_global, g_given, codes, scales, g_out, amax_out, NULL);
 }
 
-/* [R9] NVFP4 with stochastically rounded codes; rbits [rows, cols]. */
+/* [R15] NVFP4 with stochastically rounded codes; rbits [rows, cols]. */
 void bo_quantize_nvfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
                           int use_global, const float* g_given, const uint32_t* rbits,
                           uint32_t* codes, uint8_t* scales,
@@ -391,7 +391,7 @@ void bo_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols,
     quantize_mxfp4(x, rows, cols, codes, scales, NULL);
 }
 
-/* [R9] MXFP4 with stochastically rounded codes; rbits [rows, cols]. */
+/* [R15] MXFP4 with stochastically rounded codes; rbits [rows, cols]. */
 void bo_quantize_mxfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
                           const uint32_t* rbits, uint32_t* codes, uint8_t* scales)
 {

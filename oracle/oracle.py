@@ -130,7 +130,7 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
 
 
 def e2m1_encode_sr(v: float, r: int) -> int:
-    """Stochastic rounding of one fp32 value to an E2M1 code (reading R9)."""
+    """Stochastic rounding of one fp32 value to an E2M1 code (reading R15)."""
     return int(lib().bo_e2m1_encode_sr(float(np.float32(v)), int(r) & 0xFFFFFFFF))
 
 
@@ -175,7 +175,7 @@ def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
     """Quantize a bf16 [rows, cols] tensor.  For NVFP4, use_global selects a
     per-tensor global scale, either the given g or amax/2688 computed here.
     rbits (uint32 [rows, cols], NVFP4 / MXFP4 only) selects stochastic
-    rounding of the codes with those random words (reading R9)."""
+    rounding of the codes with those random words (reading R15)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x_bits.ndim == 1:
         x_bits = x_bits.reshape(1, -1)

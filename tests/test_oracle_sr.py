@@ -1,4 +1,4 @@
-"""Pins for the oracle's stochastic-rounding quantize (reading R9 of the
+"""Pins for the oracle's stochastic-rounding quantize (reading R15 of the
 oracle: the USE_SR variant of the 4-bit quantizer, "perf(cuda): enable
 hardware NVFP4/MXFP4 conversion on Blackwell builds", Current Behavior;
 the pages give no rounding rule or random-bit contract).
