@@ -30,6 +30,12 @@
  *   R7  packing: low nibble first, 8 codes per little-endian uint32.
  *   R8  dequant: NVFP4 bf16((E2M1*E4M3)*g); MXFP4 bf16(E2M1*2^e); affine
  *       bf16(fma(sb, q, bb)).
+ *   R17 MXFP8 (OCP MX v1.0, E4M3 elements): shared exponent e =
+ *       floor(log2 bamax) - 8 (448 = 1.75 * 2^8), clamped to [-127, 127];
+ *       bamax == 0 -> e = -127; elements E4M3(x * 2^-e) nearest even,
+ *       saturating at 448, sign bit kept; 4 codes per uint32, byte k mod 4.
+ *   R18 affine b-bit, group G in {32, 64, 128}: R6 with 2^b - 1 in place of
+ *       15; b = 8 packs 4 codes per uint32, byte k mod 4.
  *   R15  stochastic rounding (the USE_SR variant of the 4-bit quantizer; the
  *       pages give no rounding rule or random-bit contract): scales as in
  *       R4/R5; an element |v| strictly between grid magnitudes lo < hi
@@ -440,6 +446,142 @@ void bo_quantize_affine(const uint16_t* x, int64_t rows, int64_t cols,
             }
         }
     }
+}
+
+/* ======================================================================== */
+/* format variants [R17][R18]: generic b-bit packing                          */
+/* ======================================================================== */
+
+static void put_code_b(uint32_t* row_words, int64_t k, int code, int bits)
+{
+    const int64_t per = 32 / bits;
+    row_words[k / per] |= (uint32_t)code << (bits * (k % per));
+}
+
+static int get_code_b(const uint32_t* row_words, int64_t k, int bits)
+{
+    const int64_t per = 32 / bits;
+    return (int)((row_words[k / per] >> (bits * (k % per))) & ((1u << bits) - 1u));
+}
+
+/* Signed E4M3: sign bit 0x80, magnitude nearest even, > 448 -> 448. */
+static int e4m3_encode_signed(float v)
+{
+    return bo_e4m3_encode(fabsf(v)) | (signbit(v) ? 0x80 : 0);
+}
+
+static double e4m3_decode_signed(int c)
+{
+    double m = bo_e4m3_decode(c & 0x7F);
+    return (c & 0x80) ? -m : m;
+}
+
+/* [R18] affine b-bit quantize with group G: min/max per group, step
+ * bf16((max - min) / (2^b - 1)), bias bf16(min), codes from the stored
+ * scale and bias. */
+void bo_quantize_affine_g(const uint16_t* x, int64_t rows, int64_t cols, int bits, int G,
+                          uint32_t* codes, uint16_t* scales, uint16_t* biases)
+{
+    const float qmax = (float)((1 << bits) - 1);
+    const int64_t words = cols * bits / 32, groups = cols / G;
+    memset(codes, 0, (size_t)(rows * words) * sizeof(uint32_t));
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * cols;
+        uint32_t* cr = codes + r * words;
+        for (int64_t b = 0; b < groups; ++b) {
+            float mn = bo_bf16_to_f32(xr[b * G]), mx = mn;
+            for (int i = 1; i < G; ++i) {
+                float v = bo_bf16_to_f32(xr[b * G + i]);
+                if (v < mn) mn = v;
+                if (v > mx) mx = v;
+            }
+            float step = (mx - mn) / qmax;
+            uint16_t sb = bo_bf16_from_f32(step);
+            uint16_t bb = bo_bf16_from_f32(mn);
+            scales[r * groups + b] = sb;
+            biases[r * groups + b] = bb;
+            float s = bo_bf16_to_f32(sb), bias = bo_bf16_to_f32(bb);
+            float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+            for (int i = 0; i < G; ++i) {
+                float t = (bo_bf16_to_f32(xr[b * G + i]) - bias) * inv;
+                float q = nearbyintf(t);
+                if (q < 0.0f) q = 0.0f;
+                if (q > qmax) q = qmax;
+                put_code_b(cr, b * G + i, (int)q, bits);
+            }
+        }
+    }
+}
+
+/* [R17] MXFP8: one E8M0 exponent per 32 elements, E4M3 elements. */
+void bo_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t cols,
+                       uint32_t* codes, uint8_t* scales)
+{
+    const int G = 32;
+    const int emax_e4m3 = 8; /* largest E4M3 magnitude 448 = 1.75 * 2^8 */
+    const int64_t words = cols / 4, groups = cols / G;
+    memset(codes, 0, (size_t)(rows * words) * sizeof(uint32_t));
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * cols;
+        uint32_t* cr = codes + r * words;
+        for (int64_t b = 0; b < groups; ++b) {
+            float bamax = 0.0f;
+            for (int i = 0; i < G; ++i) {
+                float a = fabsf(bo_bf16_to_f32(xr[b * G + i]));
+                if (a > bamax) bamax = a;
+            }
+            int e = (bamax == 0.0f) ? -127 : floor_log2((double)bamax) - emax_e4m3;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            scales[r * groups + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < G; ++i) {
+                float v = ldexpf(bo_bf16_to_f32(xr[b * G + i]), -e);
+                put_code_b(cr, b * G + i, e4m3_encode_signed(v), 8);
+            }
+        }
+    }
+}
+
+/* Format variants to bf16 [R8]: affine bf16(fma(s, q, b)); MXFP8
+ * bf16(E4M3 * 2^e) with the product in fp32.  mode 0 affine, 3 MXFP8. */
+void bo_dequantize_g(int mode, int bits, int G, const uint32_t* codes, const void* scales,
+                     const uint16_t* biases, int64_t rows, int64_t cols, uint16_t* out)
+{
+    const int64_t words = cols * bits / 32, groups = cols / G;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k) {
+            int c = get_code_b(codes + r * words, k, bits);
+            if (mode == 0) {
+                const uint16_t* s16 = (const uint16_t*)scales;
+                float s = bo_bf16_to_f32(s16[r * groups + k / G]);
+                float b = bo_bf16_to_f32(biases[r * groups + k / G]);
+                out[r * cols + k] = bo_bf16_from_f32(fmaf(s, (float)c, b));
+            } else {
+                const uint8_t* s8 = (const uint8_t*)scales;
+                float t = (float)(e4m3_decode_signed(c) * bo_e8m0_decode(s8[r * groups + k / G]));
+                out[r * cols + k] = bo_bf16_from_f32(t);
+            }
+        }
+}
+
+/* Exact real values (fp64) of the format variants. */
+void bo_dequant_exact_g(int mode, int bits, int G, const uint32_t* codes, const void* scales,
+                        const uint16_t* biases, int64_t rows, int64_t cols, double* out)
+{
+    const int64_t words = cols * bits / 32, groups = cols / G;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k) {
+            int c = get_code_b(codes + r * words, k, bits);
+            if (mode == 0) {
+                const uint16_t* s16 = (const uint16_t*)scales;
+                double s = bo_bf16_to_f32(s16[r * groups + k / G]);
+                double b = bo_bf16_to_f32(biases[r * groups + k / G]);
+                out[r * cols + k] = s * c + b;
+            } else {
+                const uint8_t* s8 = (const uint8_t*)scales;
+                out[r * cols + k] = e4m3_decode_signed(c) * bo_e8m0_decode(s8[r * groups + k / G]);
+            }
+        }
 }
 
 /* ======================================================================== */

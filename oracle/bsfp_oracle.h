@@ -66,6 +66,16 @@ void bo_quantize_mxfp4_sr(const uint16_t* x, int64_t rows, int64_t cols,
 void bo_quantize_affine(const uint16_t* x, int64_t rows, int64_t cols,
                         uint32_t* codes, uint16_t* scales, uint16_t* biases);
 
+/* ---- format variants: affine b-bit group G, MXFP8 ------------------------- */
+void bo_quantize_affine_g(const uint16_t* x, int64_t rows, int64_t cols, int bits, int G,
+                          uint32_t* codes, uint16_t* scales, uint16_t* biases);
+void bo_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t cols,
+                       uint32_t* codes, uint8_t* scales);
+void bo_dequantize_g(int mode, int bits, int G, const uint32_t* codes, const void* scales,
+                     const uint16_t* biases, int64_t rows, int64_t cols, uint16_t* out);
+void bo_dequant_exact_g(int mode, int bits, int G, const uint32_t* codes, const void* scales,
+                        const uint16_t* biases, int64_t rows, int64_t cols, double* out);
+
 /* ---- dequantize to bf16 --------------------------------------------------- */
 void bo_dequantize_nvfp4(const uint32_t* codes, const uint8_t* scales,
                          const float* g /* NULL: no global scale */,

@@ -6,7 +6,9 @@ product package.  It does not import the product package and shares no code
 with it.
 
 All arrays are numpy, host side.  bf16 tensors are uint16 bit patterns.
-Modes: 0 affine (group 64), 1 MXFP4 (group 32), 2 NVFP4 (group 16).
+Modes: 0 affine (4-bit group 64; format variants: 4 or 8 bits, groups 32,
+64, 128), 1 MXFP4 (group 32), 2 NVFP4 (group 16), 3 MXFP8 (8-bit E4M3
+elements, group 32).
 """
 from __future__ import annotations
 
@@ -20,9 +22,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-AFFINE, MXFP4, NVFP4 = 0, 1, 2
-GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16}
-MODE_NAMES = {AFFINE: "affine", MXFP4: "mxfp4", NVFP4: "nvfp4"}
+AFFINE, MXFP4, NVFP4, MXFP8 = 0, 1, 2, 3
+GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16, MXFP8: 32}
+BITS = {AFFINE: 4, MXFP4: 4, NVFP4: 4, MXFP8: 8}
+MODE_NAMES = {AFFINE: "affine", MXFP4: "mxfp4", NVFP4: "nvfp4", MXFP8: "mxfp8"}
 
 _lib = None
 
@@ -63,6 +66,10 @@ def lib():
             "bo_quantize_mxfp4": (None, [_P, _I64, _I64, _P, _P]),
             "bo_quantize_nvfp4_sr": (None, [_P, _I64, _I64, C.c_int, _P, _P, _P, _P, _P, _P]),
             "bo_quantize_mxfp4_sr": (None, [_P, _I64, _I64, _P, _P, _P]),
+            "bo_quantize_affine_g": (None, [_P, _I64, _I64, C.c_int, C.c_int, _P, _P, _P]),
+            "bo_quantize_mxfp8": (None, [_P, _I64, _I64, _P, _P]),
+            "bo_dequantize_g": (None, [C.c_int, C.c_int, C.c_int, _P, _P, _P, _I64, _I64, _P]),
+            "bo_dequant_exact_g": (None, [C.c_int, C.c_int, C.c_int, _P, _P, _P, _I64, _I64, _P]),
             "bo_e2m1_encode_sr": (C.c_int, [C.c_float, C.c_uint32]),
             "bo_quantize_affine": (None, [_P, _I64, _I64, _P, _P, _P]),
             "bo_dequantize_nvfp4": (None, [_P, _P, _P, _I64, _I64, _P]),
@@ -168,10 +175,23 @@ class QTensor:
     biases: Optional[np.ndarray] = None  # uint16 bf16 [rows, cols/64], affine only
     g: Optional[np.float32] = None     # NVFP4 global scale (None: no global scale)
     amax: Optional[np.float32] = None  # NVFP4 tensor amax when computed
+    bits: int = 4                      # code width (8: affine 8-bit, MXFP8)
+    group: Optional[int] = None        # group size (None: the mode's default)
+
+    @property
+    def group_size(self) -> int:
+        return self.group if self.group is not None else GROUP[self.mode]
+
+    @property
+    def variant(self) -> bool:
+        """A format variant: MXFP8, or affine other than 4-bit group 64."""
+        return self.mode == MXFP8 or (self.mode == AFFINE and
+                                      (self.bits, self.group_size) != (4, 64))
 
 
 def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
-             g: Optional[float] = None, rbits: Optional[np.ndarray] = None) -> QTensor:
+             g: Optional[float] = None, rbits: Optional[np.ndarray] = None,
+             bits: Optional[int] = None, group: Optional[int] = None) -> QTensor:
     """Quantize a bf16 [rows, cols] tensor.  For NVFP4, use_global selects a
     per-tensor global scale, either the given g or amax/2688 computed here.
     rbits (uint32 [rows, cols], NVFP4 / MXFP4 only) selects stochastic
@@ -180,9 +200,28 @@ def quantize(mode: int, x_bits: np.ndarray, use_global: bool = True,
     if x_bits.ndim == 1:
         x_bits = x_bits.reshape(1, -1)
     rows, cols = x_bits.shape
-    G = GROUP[mode]
+    G = group if group is not None else GROUP[mode]
+    nbits = bits if bits is not None else BITS[mode]
     if cols % G:
         raise ValueError(f"cols={cols} is not a multiple of the group size {G}")
+    if mode == MXFP8:
+        if (nbits, G) != (8, 32):
+            raise ValueError("MXFP8 is 8-bit with groups of 32")
+        codes = np.zeros((rows, cols // 4), np.uint32)
+        scales = np.zeros((rows, cols // G), np.uint8)
+        lib().bo_quantize_mxfp8(_ptr(x_bits), rows, cols, _ptr(codes), _ptr(scales))
+        return QTensor(mode, rows, cols, codes, scales, bits=8, group=32)
+    if mode == AFFINE and (nbits, G) != (4, 64):
+        if nbits not in (4, 8) or G not in (32, 64, 128):
+            raise ValueError(f"affine ({nbits} bits, group {G}) is not a supported variant")
+        codes = np.zeros((rows, cols * nbits // 32), np.uint32)
+        scales = np.zeros((rows, cols // G), np.uint16)
+        biases = np.zeros((rows, cols // G), np.uint16)
+        lib().bo_quantize_affine_g(_ptr(x_bits), rows, cols, nbits, G, _ptr(codes),
+                                   _ptr(scales), _ptr(biases))
+        return QTensor(mode, rows, cols, codes, scales, biases, bits=nbits, group=G)
+    if (nbits, G) != (BITS[mode], GROUP[mode]):
+        raise ValueError(f"{MODE_NAMES[mode]} has no ({nbits} bits, group {G}) variant")
     if rbits is not None:
         if mode == AFFINE:
             raise ValueError("stochastic rounding applies to NVFP4 and MXFP4")
@@ -224,6 +263,10 @@ def dequantize(q: QTensor) -> np.ndarray:
     """bf16 bits [rows, cols] (NVFP4 includes the global scale when present)."""
     out = np.empty((q.rows, q.cols), np.uint16)
     L = lib()
+    if q.variant:
+        L.bo_dequantize_g(q.mode, q.bits, q.group_size, _ptr(q.codes), _ptr(q.scales),
+                          _ptr(q.biases), q.rows, q.cols, _ptr(out))
+        return out
     if q.mode == NVFP4:
         g = None if q.g is None else np.array([q.g], np.float32)
         L.bo_dequantize_nvfp4(_ptr(q.codes), _ptr(q.scales), _ptr(g), q.rows, q.cols, _ptr(out))
@@ -245,6 +288,10 @@ def dequant_exact(q: QTensor, with_g: bool = True, rows: Optional[np.ndarray] = 
         biases = None if biases is None else np.ascontiguousarray(biases[rows])
     nrows = codes.shape[0]
     out = np.empty((nrows, q.cols), np.float64)
+    if q.variant:
+        lib().bo_dequant_exact_g(q.mode, q.bits, q.group_size, _ptr(codes), _ptr(scales),
+                                 _ptr(biases), nrows, q.cols, _ptr(out))
+        return out
     g = None
     if q.mode == NVFP4 and with_g and q.g is not None:
         g = np.array([q.g], np.float32)
