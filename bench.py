@@ -21,6 +21,9 @@ already resident in HBM:
               dequantized exactly, then the GEMV; alpha = g_x g_w)
   qmm_mx32 / qmm_mx512   MXFP4 qq GEMM on the scaled MFMA, W[5760,2880]
   qmm_affine  affine weight-only x[2048,5120] . W_up[25600,5120]^T
+  qmv_<fmt>    decode GEMV (M = 1) on W[25600,5120] in each format variant:
+              mxfp8, affine 4-bit groups 32 / 128, affine 8-bit groups
+              32 / 64 / 128 (`qmv_variants_gbs`)
   wonly_M / dense_M   NVFP4 weight-only X[M,5120] . W[25600,5120]^T at
               M = 1134, 2048, 4096: the fused kernel (W decoded in registers)
               and the dense prefill path (W dequantized to bf16 into one
@@ -202,6 +205,24 @@ def main():
     def st_qmm_affine():
         b.qmm(X_aff, q_up0, act="bf16", out=Y_aff)
 
+    # decode GEMV in the format variants (one W[25600,5120] each)
+    VARIANTS = {"mxfp8": (b.MXFP8, 8, 32), "aff4g32": (b.AFFINE, 4, 32),
+                "aff4g128": (b.AFFINE, 4, 128), "aff8g32": (b.AFFINE, 8, 32),
+                "aff8g64": (b.AFFINE, 8, 64), "aff8g128": (b.AFFINE, 8, 128)}
+    q_var = {}
+    for i, (name, (mode, nb, G)) in enumerate(VARIANTS.items()):
+        wb = S.torch_normal_bf16((INTER, HIDDEN), 0.02, 900 + i, dev)
+        q_var[name] = b.quantize(wb, mode, bits=nb, group=G)
+        del wb
+
+    def var_bytes(name):
+        mode, nb, G = VARIANTS[name]
+        per_group = 4 if mode == b.AFFINE else 1  # bf16 scale + bias, or one E8M0 byte
+        return INTER * HIDDEN * nb // 8 + INTER * (HIDDEN // G) * per_group + HIDDEN * 2 + INTER * 2
+
+    def qmv_var(name):
+        return lambda: b.qmv(x_dec, q_var[name], out=y_nv1)
+
     # dense prefill path vs the fused weight-only kernel on the NVFP4 weights
     dense_scratch = torch.empty(b.qmm_dense_scratch_bytes(INTER, HIDDEN), dtype=torch.uint8,
                                 device=dev)
@@ -220,6 +241,7 @@ def main():
               ("qmm_affine", st_qmm_affine)]
     for M in (1134, 2048, 4096):
         stages += [(f"wonly_{M}", wonly(M)), (f"dense_{M}", dense(M))]
+    stages += [(f"qmv_{name}", qmv_var(name)) for name in VARIANTS]
     if args.only:
         keep = set(args.only.split(","))
         stages = [s for s in stages if s[0] in keep]
@@ -312,6 +334,10 @@ def main():
                 out[f"qmm_tflops_m{M}"] = round(2.0 * M * INTER * HIDDEN / (ms[key] * 1e-3) / 1e12, 1)
     if "qmm_affine" in ms:
         out["qmm_affine_tflops"] = round(2.0 * 2048 * INTER * HIDDEN / (ms["qmm_affine"] * 1e-3) / 1e12, 1)
+    var = {name: round(var_bytes(name) / (ms[f"qmv_{name}"] * 1e-3) / 1e9, 1)
+           for name in VARIANTS if f"qmv_{name}" in ms}
+    if var:
+        out["qmv_variants_gbs"] = var
     cross = {}
     for M in (1134, 2048, 4096):
         if f"dense_{M}" in ms and f"wonly_{M}" in ms:

@@ -22,8 +22,9 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsfp.so")
 
-AFFINE, MXFP4, NVFP4 = 0, 1, 2
-GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16}
+AFFINE, MXFP4, NVFP4, MXFP8 = 0, 1, 2, 3
+GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16, MXFP8: 32}
+BITS = {AFFINE: 4, MXFP4: 4, NVFP4: 4, MXFP8: 8}
 GS_NONE, GS_COMPUTE, GS_GIVEN = 0, 1, 2
 ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
@@ -118,39 +119,49 @@ class QuantizedTensor:
     mode: int
     rows: int
     cols: int
-    codes: torch.Tensor                       # int32 [rows, cols/8] (uint32 words)
+    codes: torch.Tensor                       # int32 [rows, cols*bits/32] (uint32 words)
     scales: torch.Tensor                      # uint8 [rows, cols/g] or bf16 (affine)
-    biases: Optional[torch.Tensor] = None     # bf16 [rows, cols/64] (affine)
+    biases: Optional[torch.Tensor] = None     # bf16 [rows, cols/g] (affine)
     global_scale: Optional[torch.Tensor] = None  # fp32 [1] (NVFP4 g)
     amax: Optional[torch.Tensor] = None          # fp32 [1] (NVFP4 tensor amax)
+    bits: Optional[int] = None                   # None: the mode's (4; MXFP8 8)
+    group: Optional[int] = None                  # None: the mode's group size
 
     @property
     def group_size(self) -> int:
-        return GROUP[self.mode]
+        return self.group if self.group is not None else GROUP[self.mode]
+
+    @property
+    def nbits(self) -> int:
+        return self.bits if self.bits is not None else BITS[self.mode]
 
     def desc(self) -> QTensorDesc:
         """The C descriptor; rebuilt whenever a field or a tensor's storage changed."""
         ts = (self.codes, self.scales, self.biases, self.global_scale, self.amax)
-        key = (self.mode, self.rows, self.cols) + tuple(
+        key = (self.mode, self.nbits, self.group_size, self.rows, self.cols) + tuple(
             None if t is None else t.data_ptr() for t in ts)
         cached = self.__dict__.get("_desc")
         if cached is None or cached[0] != key:
-            d = QTensorDesc(self.mode, 4, GROUP[self.mode], self.rows, self.cols, *key[3:])
+            d = QTensorDesc(*key)
             self.__dict__["_desc"] = cached = (key, d)
         return cached[1]
 
 
 def empty_quantized(mode: int, rows: int, cols: int, device="cuda",
-                    global_scale: bool = True) -> QuantizedTensor:
-    G = GROUP[mode]
+                    global_scale: bool = True, bits: Optional[int] = None,
+                    group: Optional[int] = None) -> QuantizedTensor:
+    G = group if group is not None else GROUP[mode]
+    nb = bits if bits is not None else BITS[mode]
     if cols % G:
         raise ValueError(f"cols={cols} is not a multiple of the group size {G}")
-    codes = torch.empty((rows, cols // 8), dtype=torch.int32, device=device)
+    codes = torch.empty((rows, cols * nb // 32), dtype=torch.int32, device=device)
     if mode == AFFINE:
         scales = torch.empty((rows, cols // G), dtype=torch.bfloat16, device=device)
         biases = torch.empty((rows, cols // G), dtype=torch.bfloat16, device=device)
-        return QuantizedTensor(mode, rows, cols, codes, scales, biases)
+        return QuantizedTensor(mode, rows, cols, codes, scales, biases, bits=bits, group=group)
     scales = torch.empty((rows, cols // G), dtype=torch.uint8, device=device)
+    if mode == MXFP8:
+        return QuantizedTensor(mode, rows, cols, codes, scales, bits=bits, group=group)
     gs = am = None
     if mode == NVFP4 and global_scale:
         gs = torch.empty(1, dtype=torch.float32, device=device)
@@ -181,7 +192,8 @@ def amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
 def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
              g: Optional[torch.Tensor] = None,
              out: Optional[QuantizedTensor] = None,
-             rbits: Optional[torch.Tensor] = None) -> QuantizedTensor:
+             rbits: Optional[torch.Tensor] = None, bits: Optional[int] = None,
+             group: Optional[int] = None) -> QuantizedTensor:
     """Quantize a bf16 [rows, cols] GPU tensor.  For NVFP4, global_scale is
     'compute' (g = amax/2688), 'given' (use the fp32 [1] tensor g) or 'none'.
     rbits (uint32 words, one per element, NVFP4 / MXFP4): stochastic rounding
@@ -190,7 +202,8 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
     rows, cols = x2.shape
     gs = {"none": GS_NONE, "compute": GS_COMPUTE, "given": GS_GIVEN}[global_scale]
     if out is None:
-        out = empty_quantized(mode, rows, cols, x.device, global_scale=(gs != GS_NONE))
+        out = empty_quantized(mode, rows, cols, x.device, global_scale=(gs != GS_NONE),
+                              bits=bits, group=group)
         if mode == NVFP4 and gs == GS_GIVEN:
             if g is None:
                 raise ValueError("global_scale='given' needs g")

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <mutex>
 
+#include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
 
 namespace bsfp {
@@ -40,33 +41,29 @@ bsfp_status device_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int expected_group(int mode) {
-  switch (mode) {
-    case BSFP_AFFINE: return 64;
-    case BSFP_MXFP4: return 32;
-    case BSFP_NVFP4: return 16;
-    default: return -1;
-  }
-}
-
 const char* mode_name(int mode) {
   switch (mode) {
     case BSFP_AFFINE: return "affine";
     case BSFP_MXFP4: return "mxfp4";
     case BSFP_NVFP4: return "nvfp4";
+    case BSFP_MXFP8: return "mxfp8";
     default: return "unknown";
   }
+}
+
+// A format variant (MXFP8, or affine other than 4-bit group 64).
+bool is_variant(const bsfp_qtensor* q) {
+  return format_id(q->mode, q->bits, q->group_size) >= FMT_MXFP8;
 }
 
 // Checks the descriptor of a quantized tensor; need_data: its code/scale
 // buffers must be present (non-empty tensors).
 bsfp_status check_qtensor(const bsfp_qtensor* q, const char* fn) {
   if (!q) return fail(BSFP_ERR_ARG, "%s: null tensor descriptor", fn);
-  if (q->mode < BSFP_AFFINE || q->mode > BSFP_NVFP4 || q->bits != 4 ||
-      q->group_size != expected_group(q->mode))
+  if (format_id(q->mode, q->bits, q->group_size) < 0)
     return fail(BSFP_ERR_UNSUPPORTED,
                 "%s: unsupported format (mode %d, bits %d, group %d); supported: "
-                "(affine, 4, 64), (mxfp4, 4, 32), (nvfp4, 4, 16)",
+                "(affine, 4 or 8, 32/64/128), (mxfp4, 4, 32), (nvfp4, 4, 16), (mxfp8, 8, 32)",
                 fn, (int)q->mode, (int)q->bits, (int)q->group_size);
   if (q->rows < 0 || q->cols < 0)
     return fail(BSFP_ERR_ARG, "%s: negative shape [%lld, %lld]", fn, (long long)q->rows,
@@ -187,7 +184,9 @@ static bsfp_status quantize_impl(const uint16_t* x, const bsfp_qtensor* q, int32
         e = launch_quantize_mxfp4(x, n_words, q->codes, (uint8_t*)q->scales, s, rbits);
       break;
     default:
-      if (n_words > 0)
+      if (is_variant(q))
+        e = launch_quantize_variant(x, *q, s);
+      else if (n_words > 0)
         e = launch_quantize_affine(x, n_words, q->codes, (uint16_t*)q->scales, q->biases, s);
       break;
   }
@@ -225,6 +224,11 @@ bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w, uint16
   if (w->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmv: K must be positive");
   if (!x || !aligned16(x)) return fail(BSFP_ERR_ARG, "bsfp_qmv: x is null or not 16-byte aligned");
   if (w->rows > 0 && !y) return fail(BSFP_ERR_ARG, "bsfp_qmv: null y");
+  if (is_variant(w) && !qmv_variant_supported((int)M, *w))
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_qmv: %s %d-bit group %d needs x of at most 64 KB and K < 2^28 "
+                "(M = %lld, K = %lld)", mode_name(w->mode), (int)w->bits, (int)w->group_size,
+                (long long)M, (long long)w->cols);
   return device_status(launch_qmv(x, (int)M, *w, y, (hipStream_t)stream), "bsfp_qmv");
 }
 
@@ -238,6 +242,10 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_
                      void* workspace, size_t workspace_bytes, uint16_t* y, bsfp_stream stream) {
   bsfp_status st = check_qtensor(w, "bsfp_qmm");
   if (st != BSFP_OK) return st;
+  if (is_variant(w))
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_qmm: %s %d-bit group %d runs on the dense path (bsfp_qmm_dense)",
+                mode_name(w->mode), (int)w->bits, (int)w->group_size);
   if (M < 0) return fail(BSFP_ERR_ARG, "bsfp_qmm: negative M");
   if (act != BSFP_ACT_BF16 && act != BSFP_ACT_SAME)
     return fail(BSFP_ERR_ARG, "bsfp_qmm: bad activation mode %d", (int)act);

@@ -21,6 +21,36 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------- formats
+// Kernel-side format ids: the three base formats keep their bsfp mode
+// values; the variants (MXFP8, affine 4-bit with groups 32 / 128, affine
+// 8-bit with groups 32 / 64 / 128) follow.  8-bit codes pack 4 per word,
+// element k in byte k mod 4.
+enum : int {
+  FMT_AFF4_G64 = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_MXFP8 = 3,
+  FMT_AFF4_G32 = 4, FMT_AFF4_G128 = 5, FMT_AFF8_G32 = 6, FMT_AFF8_G64 = 7, FMT_AFF8_G128 = 8
+};
+__host__ __device__ constexpr bool fmt_affine(int f) { return f == FMT_AFF4_G64 || f >= FMT_AFF4_G32; }
+__host__ __device__ constexpr int fmt_bits(int f) { return (f == FMT_MXFP8 || f >= FMT_AFF8_G32) ? 8 : 4; }
+__host__ __device__ constexpr int fmt_group(int f) {
+  return f == FMT_NVFP4 ? 16
+       : (f == FMT_MXFP4 || f == FMT_MXFP8 || f == FMT_AFF4_G32 || f == FMT_AFF8_G32) ? 32
+       : (f == FMT_AFF4_G128 || f == FMT_AFF8_G128) ? 128 : 64;
+}
+__host__ __device__ constexpr int fmt_sbytes(int f) { return fmt_affine(f) ? 2 : 1; }
+// Format id of (mode, bits, group), -1 if the library has none.
+__host__ __device__ constexpr int format_id(int mode, int bits, int group) {
+  return mode == 1 ? (bits == 4 && group == 32 ? FMT_MXFP4 : -1)
+       : mode == 2 ? (bits == 4 && group == 16 ? FMT_NVFP4 : -1)
+       : mode == 3 ? (bits == 8 && group == 32 ? FMT_MXFP8 : -1)
+       : mode != 0 ? -1
+       : bits == 4 ? (group == 64 ? FMT_AFF4_G64 : group == 32 ? FMT_AFF4_G32
+                      : group == 128 ? FMT_AFF4_G128 : -1)
+       : bits == 8 ? (group == 32 ? FMT_AFF8_G32 : group == 64 ? FMT_AFF8_G64
+                      : group == 128 ? FMT_AFF8_G128 : -1)
+       : -1;
+}
+
 // ---------------------------------------------------------------- bf16
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -80,6 +110,14 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
   w = e2m1_pack2<2>(w, v[4], v[5]);
   w = e2m1_pack2<3>(w, v[6], v[7]);
   return w;
+}
+
+// Bytes 2 HI and 2 HI + 1 of w (two E4M3 codes) -> two bf16 values, exact
+// (E4M3 has 4 significant bits).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Stochastic rounding of v to an E2M1 code with the random word r: between

@@ -58,6 +58,8 @@ hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words
                                               hipStream_t s);
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, hipStream_t s, const uint32_t* rbits = nullptr);
+// Quantize of the format variants (MXFP8, affine other than 4-bit group 64).
+hipError_t launch_quantize_variant(const uint16_t* x, const bsfp_qtensor& q, hipStream_t s);
 hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                   uint16_t* scales, uint16_t* biases, hipStream_t s);
 
@@ -72,6 +74,8 @@ hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t*
 // x's amax when w has one) while the GEMV stages it, and the products run on
 // its exact dequantization, with alpha = g_x * g_w on the output.  Applies
 // when qmv_qx_fusable(M, w) (x fits the GEMV's LDS copy, 1 <= M <= 8).
+// The format variants' GEMV needs x in one LDS copy (M * K * 2 <= 64 KB).
+bool qmv_variant_supported(int M, const bsfp_qtensor& w);
 bool qmv_qx_fusable(int M, const bsfp_qtensor& w);
 hipError_t launch_qmv_qx(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
                          hipStream_t s);

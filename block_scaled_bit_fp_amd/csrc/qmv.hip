@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void qmv_nvfp4_words_kernel(
 constexpr int kRing = 8;
 
 struct Chunk {
-  uint4 w;     // 32 codes
+  uint4 w;     // 32 codes (4-bit), or the first 16 of them (8-bit)
+  uint4 w2;    // 8-bit: codes 16..31
   uint32_t s;  // scale bits
   uint32_t b;  // affine bias bits
 };
@@ -294,7 +295,7 @@ struct Chunk {
 // plus (affine) the per-chunk sums of x [M][NJ][32] for the bias term.
 template <int MODE>
 size_t fast_lds_bytes(int M, int NJ) {
-  return (size_t)M * NJ * (2048 + (MODE == BSFP_AFFINE ? 128 : 0));
+  return (size_t)M * NJ * (2048 + (fmt_affine(MODE) ? 128 : 0));
 }
 
 // Staging of x for the fast kernel, split in two so that the x loads can go
@@ -305,11 +306,14 @@ size_t fast_lds_bytes(int M, int NJ) {
 // (kXU, or 8 for the 512-thread variants below).
 constexpr int kXU = 4;
 
-// Rows of x per launch above 2 need more registers per lane: those variants
-// run 512-thread workgroups (256 VGPRs), two per CU, staging 8 units of x per
-// thread (the same 64 KB of x at most).
-template <int MAXM> constexpr int fast_threads() { return MAXM > 2 ? 512 : 1024; }
-template <int MAXM> constexpr int fast_xu() { return MAXM > 2 ? 8 : kXU; }
+// Rows of x per launch above 2 (above 1 with 8-bit codes) need more
+// registers per lane: those variants run 512-thread workgroups (256 VGPRs),
+// two per CU, staging 8 units of x per thread (the same 64 KB of x at most).
+template <int FMT, int MAXM> constexpr bool fast_wide() {
+  return MAXM > 2 || (fmt_bits(FMT) == 8 && MAXM > 1);  // 8-bit codes hold twice the registers
+}
+template <int FMT, int MAXM> constexpr int fast_threads() { return fast_wide<FMT, MAXM>() ? 512 : 1024; }
+template <int FMT, int MAXM> constexpr int fast_xu() { return fast_wide<FMT, MAXM>() ? 8 : kXU; }
 
 template <int XU>
 __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int M, int K,
@@ -329,7 +333,9 @@ __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int
   }
 }
 
-template <bool AFF, int XU, int QXMODE>
+// SUMS: also store the per-chunk sums of x (affine bias term); REORDER:
+// store the pairs in the order the 4-bit nibble decode produces them.
+template <bool SUMS, bool REORDER, int XU, int QXMODE>
 __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[XU],
                                               uint4* __restrict__ xp, float* __restrict__ xs,
                                               float gq) {
@@ -346,11 +352,13 @@ __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[X
       if constexpr (QXMODE == BSFP_NVFP4) v = qdq_nvfp4_half_bf16(v, gq);
       if constexpr (QXMODE == BSFP_MXFP4) v = qdq_mxfp4_quarter_bf16(v);
       uint4 o = v;
-      if constexpr (AFF) {
+      if constexpr (REORDER) {
         o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
         o.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (x4, x6)
         o.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
         o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (x5, x7)
+      }
+      if constexpr (SUMS) {
         float t = bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) +
                   bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
         t = team_sum<4>(t);  // the 4 units of chunk c are 4 adjacent threads
@@ -365,9 +373,8 @@ __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[X
 // (scales, then affine biases).
 template <int MODE>
 int block_scale_bytes(int R, int K) {
-  const int gs = MODE == BSFP_AFFINE ? 64 : MODE == BSFP_MXFP4 ? 32 : 16;
-  const int srb = (K / gs) * (MODE == BSFP_AFFINE ? 2 : 1);
-  return 2 * R * srb * (MODE == BSFP_AFFINE ? 2 : 1);
+  const int srb = (K / fmt_group(MODE)) * fmt_sbytes(MODE);
+  return 2 * R * srb * (fmt_affine(MODE) ? 2 : 1);
 }
 
 // MAXM: compile-time bound on M.  R: rows per team per block.
@@ -388,17 +395,22 @@ int block_scale_bytes(int R, int K) {
 // g_x = amax(x) / 2688 over the whole x it stages and folds it into the
 // output scale (without it, g_x = 1).
 template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
-__global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
+__global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
     const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y,
     int NJ, int nblocks, int qx_amax) {
-  static_assert(!QX || MODE != BSFP_AFFINE, "qq needs a 4-bit float format");
+  static_assert(!QX || MODE == FMT_MXFP4 || MODE == FMT_NVFP4,
+                "qq needs a 4-bit float format");
   static_assert(!(SLDS && RAGGED), "staged scales need whole 32-chunk steps");
-  constexpr bool AFF = (MODE == BSFP_AFFINE);
+  // MODE is a format id: the three base formats, MXFP8 or an affine variant
+  constexpr bool AFF = fmt_affine(MODE);
+  constexpr bool MX = (MODE == FMT_MXFP4 || MODE == FMT_MXFP8);  // one E8M0 byte per chunk
+  constexpr int BITS = fmt_bits(MODE);
+  constexpr int CB = 4 * BITS;   // code bytes of a 32-element chunk
   constexpr int PJ = kRing / R;  // steps in flight
-  constexpr int gs = AFF ? 64 : (MODE == BSFP_MXFP4) ? 32 : 16;
-  constexpr int sbytes = AFF ? 2 : 1;
+  constexpr int gs = fmt_group(MODE);
+  constexpr int sbytes = fmt_sbytes(MODE);
   constexpr int sstep = 32 * 32 / gs * sbytes;  // scale bytes of one step (32 chunks)
   extern __shared__ uint4 smem[];
   uint4* xp = smem;
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
   const int wave_in_wg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int G = gridDim.x, wg = blockIdx.x;
   const int cpr = K >> 5;
-  const int rb = K >> 1;              // code bytes per row
+  const int rb = K / 8 * BITS;        // code bytes per row
   const int srb = (K / gs) * sbytes;  // scale bytes per row
   // Blocks are dealt round-robin over the workgroups (one per CU), then over
   // the waves of a workgroup: pass p of this wave takes block
@@ -428,8 +440,10 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
   int vc[R], vs[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    vc[r] = (2 * r + h) * rb + 16 * lt;
-    vs[r] = (2 * r + h) * srb + (AFF ? 2 * (lt >> 1) : (MODE == BSFP_MXFP4) ? lt : 2 * lt);
+    vc[r] = (2 * r + h) * rb + CB * lt;
+    // the chunk's scale: its group's (affine bf16, MX one byte), NVFP4 the
+    // chunk's two E4M3 bytes
+    vs[r] = (2 * r + h) * srb + (AFF ? 2 * (lt * 32 / gs) : MX ? lt : 2 * lt);
   }
 
   rsrc_t rc, rs, rbs;
@@ -460,12 +474,13 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      dst[r].w = buffer_load_u128(rc, vc[r], j * 512);
+      dst[r].w = buffer_load_u128(rc, vc[r], j * 32 * CB);
+      if constexpr (BITS == 8) dst[r].w2 = buffer_load_u128(rc, vc[r] + 16, j * 32 * CB);
       if constexpr (!SLDS) {
         if constexpr (AFF) {
           dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 0);
           dst[r].b = __builtin_amdgcn_raw_buffer_load_b16(rbs, vs[r], j * sstep, 0);
-        } else if constexpr (MODE == BSFP_MXFP4) {
+        } else if constexpr (MX) {
           dst[r].s = __builtin_amdgcn_raw_buffer_load_b8(rs, vs[r], j * sstep, 0);
         } else {
           dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 0);
@@ -482,7 +497,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
 
   // x loads first, then the first PJ steps of weights; staging x into LDS
   // then waits only for the x loads (loads complete in issue order).
-  uint4 xr[fast_xu<MAXM>()];
+  uint4 xr[fast_xu<MODE, MAXM>()];
   stage_x_load(x, M, K, NJ, xr);
   Chunk ring[PJ][R];
   int pf = 0, jf = 0;  // next step to fetch
@@ -504,7 +519,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
       // (not yet written) x area of LDS
       float a = 0.0f;
 #pragma unroll
-      for (int i = 0; i < fast_xu<MAXM>(); ++i) {
+      for (int i = 0; i < fast_xu<MODE, MAXM>(); ++i) {
         float f[8];
         unpack8(xr[i], f);  // units past the end were loaded as zeros
 #pragma unroll
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
       g *= gq;
     }
   }
-  stage_x_store<AFF, fast_xu<MAXM>(), QX ? MODE : -1>(M, NJ, xr, xp, xs, gq);
+  stage_x_store<AFF, AFF && BITS == 4, fast_xu<MODE, MAXM>(), QX ? MODE : -1>(M, NJ, xr, xp, xs, gq);
   __syncthreads();
   if (steps == 0) return;
 
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
             if constexpr (AFF) {
               sv[r] = *reinterpret_cast<const uint16_t*>(sp);
               bv[r] = *reinterpret_cast<const uint16_t*>(sp + sarea);
-            } else if constexpr (MODE == BSFP_MXFP4) {
+            } else if constexpr (MX) {
               sv[r] = *sp;
             } else {
               sv[r] = *reinterpret_cast<const uint16_t*>(sp);
@@ -572,7 +587,40 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const uint4 w = ring[u][r].w;
-            if constexpr (AFF) {
+            if constexpr (AFF && BITS == 8) {
+              // 8-bit affine: q = lo + 16 hi over the two nibble planes of
+              // each byte, each converted exactly (E4M3 byte trick); x in
+              // natural order, element k of a word in byte k % 4
+              const uint4 w2 = ring[u][r].w2;
+              const uint32_t ww[8] = {w.x, w.y, w.z, w.w, w2.x, w2.y, w2.z, w2.w};
+              const uint32_t xx[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                       x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+              float Dl = 0.0f, Dh = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const uint32_t lo = ww[q] & 0x0F0F0F0Fu, hi = (ww[q] >> 4) & 0x0F0F0F0Fu;
+                Dl = dot2_bf16(xx[2 * q], nibbles_to_bf16x2<false>(lo), Dl);
+                Dl = dot2_bf16(xx[2 * q + 1], nibbles_to_bf16x2<true>(lo), Dl);
+                Dh = dot2_bf16(xx[2 * q], nibbles_to_bf16x2<false>(hi), Dh);
+                Dh = dot2_bf16(xx[2 * q + 1], nibbles_to_bf16x2<true>(hi), Dh);
+              }
+              acc[r][m] = __builtin_fmaf(__uint_as_float(sv[r] << 16),
+                                         __builtin_fmaf(16.0f, Dh, Dl), acc[r][m]);
+              acc[r][m] = __builtin_fmaf(__uint_as_float(bv[r] << 16), xsum, acc[r][m]);
+            } else if constexpr (MODE == FMT_MXFP8) {
+              // E4M3 bytes -> bf16 pairs (exact), one E8M0 scale per chunk
+              const uint4 w2 = ring[u][r].w2;
+              const uint32_t ww[8] = {w.x, w.y, w.z, w.w, w2.x, w2.y, w2.z, w2.w};
+              const uint32_t xx[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                       x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+              float D = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                D = dot2_bf16(xx[2 * q], e4m3x2_to_bf16x2<false>(ww[q]), D);
+                D = dot2_bf16(xx[2 * q + 1], e4m3x2_to_bf16x2<true>(ww[q]), D);
+              }
+              acc[r][m] = __builtin_fmaf(D, e8m0_decode(sv[r]), acc[r][m]);
+            } else if constexpr (AFF) {
               float D0 = 0.0f, D1 = 0.0f;
               const uint64_t h01 = (((uint64_t)w.y << 32) | w.x) >> 4;
               const uint64_t h23 = (((uint64_t)w.w << 32) | w.z) >> 4;
@@ -616,7 +664,7 @@ __global__ __launch_bounds__(fast_threads<MAXM>()) void qmv_fast_kernel(
               D1 = dot2_bf16(x3.y, e2m1x2_to_bf16x2<1>(w.w), D1);
               D1 = dot2_bf16(x3.z, e2m1x2_to_bf16x2<2>(w.w), D1);
               D1 = dot2_bf16(x3.w, e2m1x2_to_bf16x2<3>(w.w), D1);
-              if constexpr (MODE == BSFP_MXFP4) {
+              if constexpr (MODE == FMT_MXFP4) {
                 acc[r][m] = __builtin_fmaf(D0 + D1, e8m0_decode(sv[r]), acc[r][m]);
               } else {
                 // both E4M3 block scales with the hardware converter (exact)
@@ -696,8 +744,8 @@ struct FastShape {
 
 template <int MODE, int MAXM, int R, bool SLDS>
 FastShape fast_shape(int M, int K, int NJ, int64_t N) {
-  constexpr int kMaxW = fast_threads<MAXM>() / 64, kXu = fast_xu<MAXM>();
-  constexpr int kPerCu = 1024 / fast_threads<MAXM>();  // workgroups per CU
+  constexpr int kMaxW = fast_threads<MODE, MAXM>() / 64, kXu = fast_xu<MODE, MAXM>();
+  constexpr int kPerCu = 1024 / fast_threads<MODE, MAXM>();  // workgroups per CU
   const int cus = device_cu_count();
   const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
   const int units = M * NJ * 128;
@@ -754,10 +802,39 @@ bool fast_ok(int M, int NJ) {
 template <int MODE, int R>
 bool slds_ok(int K, int NJ, int M, int64_t N) {
   const int cpr = K / 32;
-  const int sarea = block_scale_bytes<MODE>(R, K) / (MODE == BSFP_AFFINE ? 2 : 1);
+  const int sarea = block_scale_bytes<MODE>(R, K) / (fmt_affine(MODE) ? 2 : 1);
   const int srb = sarea / (2 * R);
   if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || kRing / R > NJ) return false;
   return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
+}
+
+// The format variants: the same kernel with fewer launch shapes (4-row
+// teams with staged scales for tall M = 1 matrices, else single rows), and
+// x always in one LDS copy (callers check qmv_variant_supported).
+template <int FMT>
+hipError_t by_m_variant(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
+                        hipStream_t s) {
+  const int K = (int)w.cols;
+  const int NJ = (int)((w.cols / 32 + 31) / 32);
+  const bool ragged = (w.cols / 32) % 32 != 0;
+  if (!fast_ok<FMT>(M, NJ)) return hipErrorNotSupported;
+  const int64_t N = w.rows;
+  if (M == 1) {
+    if (N >= 64LL * device_cu_count() && slds_ok<FMT, 4>(K, NJ, M, N))
+      return launch_fast<FMT, 1, 4, false, true, false>(x, M, w, nullptr, y, NJ, s, 0);
+    if (slds_ok<FMT, 1>(K, NJ, M, N))
+      return launch_fast<FMT, 1, 1, false, true, false>(x, M, w, nullptr, y, NJ, s, 0);
+    if (ragged) return launch_fast<FMT, 1, 1, true, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+    return launch_fast<FMT, 1, 1, false, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+  }
+  if (ragged) {
+    if (M == 2) return launch_fast<FMT, 2, 1, true, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+    if (M <= 4) return launch_fast<FMT, 4, 1, true, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+    return launch_fast<FMT, 8, 1, true, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+  }
+  if (M == 2) return launch_fast<FMT, 2, 1, false, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+  if (M <= 4) return launch_fast<FMT, 4, 1, false, false, false>(x, M, w, nullptr, y, NJ, s, 0);
+  return launch_fast<FMT, 8, 1, false, false, false>(x, M, w, nullptr, y, NJ, s, 0);
 }
 
 template <int MODE, bool QX = false>
@@ -801,6 +878,13 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
 
 }  // namespace
 
+bool qmv_variant_supported(int M, const bsfp_qtensor& w) {
+  if (w.cols % 32 != 0 || w.cols >= (1 << 28) || w.rows >= (1 << 30) || M < 1 || M > 8)
+    return false;
+  const int NJ = (int)((w.cols / 32 + 31) / 32);
+  return fast_ok<FMT_MXFP8>(M, NJ) && fast_ok<FMT_AFF8_G64>(M, NJ);
+}
+
 bool qmv_qx_fusable(int M, const bsfp_qtensor& w) {
   if (w.cols % 32 != 0 || w.cols >= (1 << 28) || w.rows >= (1 << 30) || M < 1 || M > 8)
     return false;
@@ -831,10 +915,17 @@ hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t*
                          w.rows, w.codes, (const uint8_t*)w.scales, w.global_scale, g2, y);
     return hipGetLastError();
   }
-  switch (w.mode) {
-    case BSFP_AFFINE: return by_m<BSFP_AFFINE>(x, M, w, g2, y, s);
-    case BSFP_MXFP4: return by_m<BSFP_MXFP4>(x, M, w, g2, y, s);
-    default: return by_m<BSFP_NVFP4>(x, M, w, g2, y, s);
+  switch (format_id(w.mode, w.bits, w.group_size)) {
+    case FMT_AFF4_G64: return by_m<FMT_AFF4_G64>(x, M, w, g2, y, s);
+    case FMT_MXFP4: return by_m<FMT_MXFP4>(x, M, w, g2, y, s);
+    case FMT_NVFP4: return by_m<FMT_NVFP4>(x, M, w, g2, y, s);
+    case FMT_MXFP8: return by_m_variant<FMT_MXFP8>(x, M, w, y, s);
+    case FMT_AFF4_G32: return by_m_variant<FMT_AFF4_G32>(x, M, w, y, s);
+    case FMT_AFF4_G128: return by_m_variant<FMT_AFF4_G128>(x, M, w, y, s);
+    case FMT_AFF8_G32: return by_m_variant<FMT_AFF8_G32>(x, M, w, y, s);
+    case FMT_AFF8_G64: return by_m_variant<FMT_AFF8_G64>(x, M, w, y, s);
+    case FMT_AFF8_G128: return by_m_variant<FMT_AFF8_G128>(x, M, w, y, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -287,6 +287,133 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   }
 }
 
+// ------------------------------------------------------ format variants
+
+// Affine b-bit quantize with group G (4-bit group 64 is
+// quantize_affine_kernel; same steps with 2^b - 1 levels): a lane owns 8
+// elements, a group is G / 8 adjacent lanes.  8-bit codes go out as two
+// words per lane (element k in byte k % 4).
+template <int BITS, int G>
+__global__ __launch_bounds__(kThreads) void quantize_affine_g_kernel(
+    const uint4* __restrict__ x, int64_t n_units, uint32_t* __restrict__ codes,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ biases) {
+  constexpr int TEAM = G / 8;
+  constexpr float QMAX = (float)((1 << BITS) - 1);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of TEAM
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_units; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float mn = f[0], mx = f[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) { mn = fminf(mn, f[k]); mx = fmaxf(mx, f[k]); }
+    mn = team_min<TEAM>(mn);
+    mx = team_max<TEAM>(mx);
+    const float step = (mx - mn) / QMAX;
+    const uint32_t sb = f32_to_bf16(step);
+    const uint32_t bb = __float_as_uint(mn) >> 16;  // mn is a bf16 value: exact
+    const float sc = __uint_as_float(sb << 16);
+    const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+    uint32_t q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float t = __builtin_rintf((f[k] - mn) * inv);
+      q[k] = (uint32_t)fminf(fmaxf(t, 0.0f), QMAX);
+    }
+    if constexpr (BITS == 4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w |= q[k] << (4 * k);
+      codes[i] = w;
+    } else {
+      reinterpret_cast<uint2*>(codes)[i] =
+          make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                     q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+    }
+    if (i % TEAM == 0) {
+      scales[i / TEAM] = (uint16_t)sb;
+      biases[i / TEAM] = (uint16_t)bb;
+    }
+  }
+}
+
+// MXFP8 (OCP MX, E4M3 elements): e = floor(log2 amax) - 8 per 32 elements
+// (4 lanes), clamped to [-127, 127]; elements E4M3(x * 2^-e), nearest even,
+// saturating at 448, sign bit kept.
+__global__ __launch_bounds__(kThreads) void quantize_mxfp8_kernel(
+    const uint4* __restrict__ x, int64_t n_units, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_units; i += stride) {
+    float f[8];
+    unpack8(x[i], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+    a = team_max<4>(a);
+    // floor(log2 a) = biased exponent - 127 for normal a; subnormal or zero
+    // a gives an exponent below -127 after the - 8, which the clamp maps to
+    // -127
+    const int be = (int)(__float_as_uint(a) >> 23);
+    const int e = max(be - 135, -127);
+    const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = f[k] * p;
+      c[k] = e4m3_encode(fabsf(v)) | ((__float_as_uint(v) >> 31) << 7);
+    }
+    codes[i] = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                          c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+  }
+}
+
+// Format variants to bf16: affine bf16(fma(s, q, b)); MXFP8 bf16(E4M3 *
+// 2^e) with the product in fp32 (exact unless below fp32's normal range,
+// then one rounding).  8 elements per lane.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequantize_g_kernel(
+    const uint32_t* __restrict__ codes, const void* __restrict__ scales,
+    const uint16_t* __restrict__ biases, int64_t n_units, uint4* __restrict__ out) {
+  constexpr int BITS = fmt_bits(FMT), UPG = fmt_group(FMT) / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_units; i += stride) {
+    float v[8];
+    if constexpr (BITS == 4) {
+      const uint32_t w = codes[i];
+      const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[i / UPG]);
+      const float b = bf16_to_f32(biases[i / UPG]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(s, (float)((w >> (4 * k)) & 15u), b);
+    } else {
+      const uint2 w = reinterpret_cast<const uint2*>(codes)[i];
+      if constexpr (FMT == FMT_MXFP8) {
+        const float sc = e8m0_decode(reinterpret_cast<const uint8_t*>(scales)[i >> 2]);
+        const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, false);
+        const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, true);
+        const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, false);
+        const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, true);
+        v[0] = p0.x * sc; v[1] = p0.y * sc; v[2] = p1.x * sc; v[3] = p1.y * sc;
+        v[4] = p2.x * sc; v[5] = p2.y * sc; v[6] = p3.x * sc; v[7] = p3.y * sc;
+      } else {
+        const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[i / UPG]);
+        const float b = bf16_to_f32(biases[i / UPG]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t q = ((k < 4 ? w.x : w.y) >> (8 * (k & 3))) & 255u;
+          v[k] = __builtin_fmaf(s, (float)q, b);
+        }
+      }
+    }
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    out[i] = o;
+  }
+}
+
 // Grid for a flat streaming kernel: enough workgroups to fill every CU
 // several times over, no more than the work needs.
 int stream_grid(int64_t items) {
@@ -358,11 +485,77 @@ hipError_t launch_quantize_affine(const uint16_t* x, int64_t n_words, uint32_t* 
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_variant(const uint16_t* x, const bsfp_qtensor& q, hipStream_t s) {
+  const int64_t n_units = q.rows * q.cols / 8;
+  if (n_units == 0) return hipGetLastError();
+  const dim3 grid(stream_grid(n_units)), block(kThreads);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint16_t* sc = reinterpret_cast<uint16_t*>(q.scales);
+  switch (format_id(q.mode, q.bits, q.group_size)) {
+    case FMT_MXFP8:
+      hipLaunchKernelGGL(quantize_mxfp8_kernel, grid, block, 0, s, xv, n_units,
+                         reinterpret_cast<uint2*>(q.codes), (uint8_t*)q.scales);
+      break;
+    case FMT_AFF4_G32:
+      hipLaunchKernelGGL((quantize_affine_g_kernel<4, 32>), grid, block, 0, s, xv, n_units,
+                         q.codes, sc, q.biases);
+      break;
+    case FMT_AFF4_G128:
+      hipLaunchKernelGGL((quantize_affine_g_kernel<4, 128>), grid, block, 0, s, xv, n_units,
+                         q.codes, sc, q.biases);
+      break;
+    case FMT_AFF8_G32:
+      hipLaunchKernelGGL((quantize_affine_g_kernel<8, 32>), grid, block, 0, s, xv, n_units,
+                         q.codes, sc, q.biases);
+      break;
+    case FMT_AFF8_G64:
+      hipLaunchKernelGGL((quantize_affine_g_kernel<8, 64>), grid, block, 0, s, xv, n_units,
+                         q.codes, sc, q.biases);
+      break;
+    case FMT_AFF8_G128:
+      hipLaunchKernelGGL((quantize_affine_g_kernel<8, 128>), grid, block, 0, s, xv, n_units,
+                         q.codes, sc, q.biases);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s) {
   const int64_t n_words = q.rows * q.cols / 8;
   if (n_words == 0) return hipGetLastError();
   const dim3 grid(stream_grid(n_words)), block(kThreads);
   uint4* o = reinterpret_cast<uint4*>(out);
+  const int fmt = format_id(q.mode, q.bits, q.group_size);
+  switch (fmt) {
+    case FMT_MXFP8:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_MXFP8>, grid, block, 0, s, q.codes, q.scales,
+                         nullptr, n_words, o);
+      return hipGetLastError();
+    case FMT_AFF4_G32:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_AFF4_G32>, grid, block, 0, s, q.codes,
+                         q.scales, q.biases, n_words, o);
+      return hipGetLastError();
+    case FMT_AFF4_G128:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_AFF4_G128>, grid, block, 0, s, q.codes,
+                         q.scales, q.biases, n_words, o);
+      return hipGetLastError();
+    case FMT_AFF8_G32:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_AFF8_G32>, grid, block, 0, s, q.codes,
+                         q.scales, q.biases, n_words, o);
+      return hipGetLastError();
+    case FMT_AFF8_G64:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_AFF8_G64>, grid, block, 0, s, q.codes,
+                         q.scales, q.biases, n_words, o);
+      return hipGetLastError();
+    case FMT_AFF8_G128:
+      hipLaunchKernelGGL(dequantize_g_kernel<FMT_AFF8_G128>, grid, block, 0, s, q.codes,
+                         q.scales, q.biases, n_words, o);
+      return hipGetLastError();
+    default:
+      break;
+  }
   switch (q.mode) {
     case BSFP_AFFINE:
       hipLaunchKernelGGL(dequantize_kernel<BSFP_AFFINE>, grid, block, 0, s, q.codes, q.scales,

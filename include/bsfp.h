@@ -1,9 +1,11 @@
 /*
- * bsfp.h -- C ABI of libbsfp: block-scaled 4-bit quantization and quantized
- * matmul on AMD Instinct MI355X (gfx950).
+ * bsfp.h -- C ABI of libbsfp: block-scaled 4-bit (and 8-bit) quantization
+ * and quantized matmul on AMD Instinct MI355X (gfx950).
  *
- * Formats (the contract; element k of a row is nibble k%8 of uint32 word k/8,
- * low nibble first; every tensor row-major and contiguous):
+ * Formats (the contract; with b = bits, element k of a row sits at bit
+ * b*(k % (32/b)) of uint32 word k/(32/b): for 4 bits nibble k%8 of word k/8,
+ * low nibble first, for 8 bits byte k%4 of word k/4; every tensor row-major
+ * and contiguous):
  *
  *   BSFP_NVFP4  bits 4, group 16.  codes: E2M1 (FP4) packed 8 per uint32.
  *               scales: uint8 E4M3 (OCP E4M3FN) per 16-element group.
@@ -22,8 +24,19 @@
  *               bf16 per group.  Value = s*q + b.
  *               (affine 4-bit / group 64: "epic: NVIDIA Volta (sm_70)
  *               inference acceleration program", Baseline.)
+ * Format variants ("feat(quant): backend quantization capability table
+ * ...", Context: the affine 4/8-bit and mxfp8 modes a ROCm backend runs;
+ * Gate impact: its GEMV groups 32, 64, 128):
+ *   BSFP_AFFINE bits 4 or 8, group 32, 64 or 128.  codes unsigned
+ *               0..2^bits-1.  Value = s*q + b.
+ *   BSFP_MXFP8  bits 8, group 32.  codes: E4M3 (OCP E4M3FN) bytes.  scales:
+ *               uint8 E8M0.  Value = E4M3(c) * 2^(S-127).
+ *   Entry points: bsfp_quantize, bsfp_dequantize, bsfp_qmv (x of at most
+ *   64 KB, M * K * 2 bytes) and bsfp_qmm_dense take every format;
+ *   bsfp_qmm takes the three base formats, bsfp_quantize_sr NVFP4 and
+ *   MXFP4.  Elsewhere a variant returns BSFP_ERR_UNSUPPORTED.
  *
- *   Codes and scales are uint32 [rows, cols/8] and [rows, cols/group]; the
+ *   Codes and scales are uint32 [rows, cols*bits/32] and [rows, cols/group]; the
  *   packed shape follows quantize_input in "mlx 0.30.7.3 -> 0.30.7.6"
  *   (qqmm.cpp): last dim = cols*bits/32.  Scales are linear (not the tiled
  *   layout that file builds for cuBLASLt).
@@ -34,6 +47,9 @@
  *   NVFP4  S = E4M3(bamax / (6*g)), codes = E2M1(x * (1 / (E4M3(S)*g)))
  *   MXFP4  e = floor(log2 bamax) - 2, codes = E2M1(x * 2^-e), S = e + 127
  *   AFFINE s = bf16((max-min)/15), b = bf16(min), q = rint((x-b)/s) in 0..15
+ *          (b bits: 2^b - 1 in place of 15)
+ *   MXFP8  e = floor(log2 bamax) - 8, codes = E4M3(x * 2^-e) (saturating at
+ *          448, sign bit kept), S = e + 127 (OCP MX v1.0 for E4M3 elements)
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers of the current HIP device, 16-byte
@@ -44,7 +60,7 @@
  *     with no host synchronization.
  *   - Functions never throw and never abort.  Argument errors are detected on
  *     the host before anything is enqueued and return BSFP_ERR_ARG; a
- *     format outside the three above returns BSFP_ERR_UNSUPPORTED; a failed
+ *     format outside the ones above returns BSFP_ERR_UNSUPPORTED; a failed
  *     launch returns BSFP_ERR_DEVICE.  bsfp_last_error() then describes it.
  *     (A C++ exception crossing a language bridge terminates the process, and
  *     an unsupported group size that throws aborts a whole test binary:
@@ -60,7 +76,7 @@
 extern "C" {
 #endif
 
-typedef enum { BSFP_AFFINE = 0, BSFP_MXFP4 = 1, BSFP_NVFP4 = 2 } bsfp_mode;
+typedef enum { BSFP_AFFINE = 0, BSFP_MXFP4 = 1, BSFP_NVFP4 = 2, BSFP_MXFP8 = 3 } bsfp_mode;
 
 typedef enum {
     BSFP_OK = 0,

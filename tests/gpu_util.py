@@ -27,7 +27,8 @@ def qt_to_oracle(o, q):
     scales = from_dev(q.scales) if q.mode == o.AFFINE else u8(q.scales)
     biases = from_dev(q.biases) if q.biases is not None else None
     g = None if q.global_scale is None else np.float32(q.global_scale.cpu().item())
-    return o.QTensor(q.mode, q.rows, q.cols, words(q.codes), scales, biases, g)
+    return o.QTensor(q.mode, q.rows, q.cols, words(q.codes), scales, biases, g,
+                     bits=q.nbits, group=q.group_size)
 
 
 def oracle_to_dev(b, o, qo):
@@ -42,4 +43,5 @@ def oracle_to_dev(b, o, qo):
     gs = None
     if qo.g is not None:
         gs = torch.tensor([float(qo.g)], dtype=torch.float32).cuda()
-    return b.QuantizedTensor(qo.mode, qo.rows, qo.cols, codes, scales, biases, gs, None)
+    return b.QuantizedTensor(qo.mode, qo.rows, qo.cols, codes, scales, biases, gs, None,
+                             bits=qo.bits, group=qo.group_size)

@@ -63,16 +63,34 @@ def status(blib, rc):
     return blib.STATUS[rc], blib.lib().bsfp_last_error().decode()
 
 
-@pytest.mark.parametrize("mode,bits,group", [(3, 4, 16), (2, 8, 16), (2, 4, 32), (1, 4, 16),
-                                             (0, 4, 32), (0, 4, 128), (-1, 4, 64)])
+@pytest.mark.parametrize("mode,bits,group", [(3, 4, 16), (3, 8, 16), (2, 8, 16), (2, 4, 32),
+                                             (1, 4, 16), (1, 8, 32), (0, 4, 16), (0, 8, 256),
+                                             (0, 2, 64), (4, 4, 32), (-1, 4, 64)])
 def test_unsupported_formats_are_reported_not_thrown(blib, mode, bits, group):
     d = desc(blib, mode, bits, group)
     rc = blib.lib().bsfp_quantize(C.c_void_p(FAKE), C.byref(d), 0, None)
     st, msg = status(blib, rc)
     assert st == "BSFP_ERR_UNSUPPORTED"
-    assert "supported" in msg and "(nvfp4, 4, 16)" in msg
+    assert "supported" in msg and "(nvfp4, 4, 16)" in msg and "(mxfp8, 8, 32)" in msg
     rc = blib.lib().bsfp_qmv(C.c_void_p(FAKE), 1, C.byref(d), C.c_void_p(FAKE), None)
     assert status(blib, rc)[0] == "BSFP_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("mode,bits,group", [(3, 8, 32), (0, 4, 32), (0, 4, 128), (0, 8, 32),
+                                             (0, 8, 64), (0, 8, 128)])
+def test_format_variants_routing(blib, mode, bits, group):
+    """Variants pass the descriptor check; bsfp_qmm sends them to the dense
+    path and bsfp_qmv rejects an x beyond its 64 KB LDS copy, both before
+    anything is launched."""
+    L = blib.lib()
+    d = desc(blib, mode, bits, group, rows=4, cols=256, biases=FAKE if mode == 0 else None)
+    rc = L.bsfp_qmm(C.c_void_p(FAKE), 4, C.byref(d), 0, None, 0, C.c_void_p(FAKE), None)
+    st, msg = status(blib, rc)
+    assert st == "BSFP_ERR_UNSUPPORTED" and "bsfp_qmm_dense" in msg
+    big = desc(blib, mode, bits, group, rows=4, cols=32768, biases=FAKE if mode == 0 else None)
+    rc = L.bsfp_qmv(C.c_void_p(FAKE), 2, C.byref(big), C.c_void_p(FAKE), None)
+    st, msg = status(blib, rc)
+    assert st == "BSFP_ERR_UNSUPPORTED" and "64 KB" in msg
 
 
 def test_bad_arguments(blib):
