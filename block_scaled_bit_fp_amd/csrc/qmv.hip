@@ -808,7 +808,7 @@ bool slds_ok(int K, int NJ, int M, int64_t N) {
   return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
 }
 
-// The format variants: the same kernel with fewer launch shapes (4-row
+// The format variants: the same kernel with fewer launch shapes (2-row
 // teams with staged scales for tall M = 1 matrices, else single rows), and
 // x always in one LDS copy (callers check qmv_variant_supported).
 template <int FMT>
@@ -820,8 +820,8 @@ hipError_t by_m_variant(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_
   if (!fast_ok<FMT>(M, NJ)) return hipErrorNotSupported;
   const int64_t N = w.rows;
   if (M == 1) {
-    if (N >= 64LL * device_cu_count() && slds_ok<FMT, 4>(K, NJ, M, N))
-      return launch_fast<FMT, 1, 4, false, true, false>(x, M, w, nullptr, y, NJ, s, 0);
+    if (N >= 32LL * device_cu_count() && slds_ok<FMT, 2>(K, NJ, M, N))
+      return launch_fast<FMT, 1, 2, false, true, false>(x, M, w, nullptr, y, NJ, s, 0);
     if (slds_ok<FMT, 1>(K, NJ, M, N))
       return launch_fast<FMT, 1, 1, false, true, false>(x, M, w, nullptr, y, NJ, s, 0);
     if (ragged) return launch_fast<FMT, 1, 1, true, false, false>(x, M, w, nullptr, y, NJ, s, 0);
@@ -845,11 +845,11 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
   const bool ragged = (w.cols / 32) % 32 != 0;
   if (fast_ok<MODE>(M, NJ) && w.cols < (1 << 28) && w.rows < (1 << 30)) {
     if (M == 1) {
-      // the largest block (rows per team) that still gives every CU 8 waves
+      // two rows per team once that still gives every CU 8 waves (measured
+      // faster than four rows per team on the [25600, 5120] shape, where
+      // both fill the CUs)
       const int64_t want = 8LL * device_cu_count();
       const int64_t N = w.rows;
-      if (N >= 8 * want && slds_ok<MODE, 4>(K, NJ, M, N))
-        return launch_fast<MODE, 1, 4, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
       if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, M, N))
         return launch_fast<MODE, 1, 2, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
       if (slds_ok<MODE, 1>(K, NJ, M, N)) return launch_fast<MODE, 1, 1, false, true, QX>(x, M, w, g2, y, NJ, s, qx_amax);
