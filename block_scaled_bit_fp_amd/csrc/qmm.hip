@@ -540,26 +540,31 @@ hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float
 // kernel above: half h takes pieces 4h .. 4h+3, op_sel picks the scale byte.
 // The last, partial unit loads only its 2J pieces (the rest come back as
 // zeros) and takes its scales, masked to the valid blocks, straight from
-// memory.  Three stages rotate with one barrier per unit, as in the bf16 GEMM.
-template <int WM, int WN, int KS, int WMT, int WNT>
+// memory.  NS stages rotate with one barrier per unit, the loads of NS - 1
+// units in flight.
+template <int WM, int WN, int KS, int WMT, int WNT, int NS>
 struct MxlCfg {
   static constexpr int GW = WM * WN;  // waves per k-group
   static constexpr int NW = GW * KS;
   static constexpr int BM = 32 * WMT * WM, BN = 32 * WNT * WN, R = BM + BN;
-  static constexpr int CODE_B = R * 128, GROUP_B = R * 136;
+  // scale rows padded to whole 32-row loads per wave (the padding loads out
+  // of range and is never read)
+  static constexpr int RS = (R + 32 * GW - 1) / (32 * GW) * (32 * GW);
+  static constexpr int CODE_B = R * 128, GROUP_B = R * 128 + RS * 8;
   static constexpr int STAGE_B = KS * GROUP_B;
-  static constexpr int CIW = R / 8 / GW, SIW = R / 32 / GW;  // loads per wave per stage
-  static constexpr int LDS = 3 * STAGE_B;
-  static_assert(R % (32 * GW) == 0, "whole scale loads per wave");
+  static constexpr int CIW = R / 8 / GW, SIW = RS / 32 / GW;  // loads per wave per stage
+  static constexpr int LDS = NS * STAGE_B;
+  static_assert(R % (8 * GW) == 0, "whole 8-row code loads per wave");
+  static_assert(NS >= 3 && NS <= 5, "stage ring");
   static_assert((KS - 1) * GW * WMT * WNT * 4096 <= LDS, "reduction fits the ring");
 };
 
-template <int WM, int WN, int KS, int WMT, int WNT>
+template <int WM, int WN, int KS, int WMT, int WNT, int NS>
 __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
     const uint32_t* __restrict__ xc, const uint8_t* __restrict__ xs,
     const uint32_t* __restrict__ wc, const uint8_t* __restrict__ wsc, int M, int N, int K,
     uint16_t* __restrict__ Y, int tiles_m, int tiles_n, int units_per_split) {
-  using C = MxlCfg<WM, WN, KS, WMT, WNT>;
+  using C = MxlCfg<WM, WN, KS, WMT, WNT, NS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int kOff = 0x40000000;  // beyond every window: loads return 0
   const int lane = threadIdx.x & 63;
@@ -600,7 +605,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
   for (int s = 0; s < C::SIW; ++s) {
     const int row = 32 * (wg * C::SIW + s) + (lane >> 1);
     const int r = row < C::BM ? row : row - C::BM;
-    s_off[s] = r * sb + 4 * (lane & 1);
+    s_off[s] = row < C::R ? r * sb + 4 * (lane & 1) : kOff;  // padding rows: out of range
   }
   auto group_base = [&](int slot) { return lds + slot * C::STAGE_B + ks * C::GROUP_B; };
 
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
     const int so = valid ? u * 8 : kOff;
 #pragma unroll
     for (int s = 0; s < C::SIW; ++s) {
-      const bool isA = 32 * (wg * C::SIW + s) < C::BM;
+      const bool isA = 32 * (wg * C::SIW + s) < C::BM;  // padding rows sit past B
       buffer_load_lds4(isA ? rxs : rws, base + C::CODE_B + (wg * C::SIW + s) * 256,
                        s_off[s] + so, 0);
     }
@@ -742,15 +747,22 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
   // every wave runs the same number of stages (units_per_split); a k-group
   // past its last unit loads out of range and skips the MFMAs
   const int nst = units_per_split;
-  load_stage(0, 0);
-  if (nst > 1) load_stage(1, 1);
+  constexpr int L = C::CIW + C::SIW;  // loads per stage and wave
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nst) load_stage(p, p);
   for (int t = 0; t < nst; ++t) {
-    if (t + 1 < nst) wait_vmem_le<C::CIW + C::SIW>();
+    // stage t must have landed; the min(NS - 2, nst - 1 - t) stages after it
+    // may stay in flight
+    const int ahead = min(NS - 2, nst - 1 - t);
+    if (ahead >= NS - 2) wait_vmem_le<(NS - 2) * L>();
+    else if (ahead >= 2) wait_vmem_le<2 * L>();
+    else if (ahead == 1) wait_vmem_le<L>();
     else wait_vmem();
     __syncthreads();
-    if (t + 2 < nst) load_stage(t + 2, (t + 2) % 3);
+    if (t + NS - 1 < nst) load_stage(t + NS - 1, (t + NS - 1) % NS);
     if (t == 0) load_tail_scales();
-    compute(t, t % 3);
+    compute(t, t % NS);
   }
 
   if (kSplitAcc) {
@@ -795,10 +807,10 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
     }
 }
 
-template <int WM, int WN, int KS, int WMT, int WNT>
+template <int WM, int WN, int KS, int WMT, int WNT, int NS>
 hipError_t launch_mxl(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtensor& w,
                       uint16_t* y, hipStream_t s) {
-  using C = MxlCfg<WM, WN, KS, WMT, WNT>;
+  using C = MxlCfg<WM, WN, KS, WMT, WNT, NS>;
   const int N = (int)w.rows, K = (int)w.cols;
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
@@ -812,13 +824,13 @@ hipError_t launch_mxl(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_q
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (!granted[dev].load(std::memory_order_relaxed)) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT>),
+          reinterpret_cast<const void*>(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT, NS>),
           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
       if (e != hipSuccess) return e;
       granted[dev].store(true, std::memory_order_relaxed);
     }
   }
-  launch_main(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT>, dim3(tiles_m * tiles_n), dim3(64 * C::NW),
+  launch_main(&gemm_mxl_kernel<WM, WN, KS, WMT, WNT, NS>, dim3(tiles_m * tiles_n), dim3(64 * C::NW),
               (uint32_t)C::LDS, s, xc, xs, w.codes, (const uint8_t*)w.scales, M, N, K, y, tiles_m,
               tiles_n, ups);
   return hipGetLastError();
@@ -829,8 +841,8 @@ hipError_t run_mx(const uint32_t* xc, const uint8_t* xs, int M, const bsfp_qtens
   // few rows: one 32 x 32 tile per workgroup with K split over 4 waves, so
   // the N / 32 workgroups still carry 4 waves each; otherwise 128 x 128 tiles
   // on 8 waves (64 x 32 per wave)
-  if (M <= 64) return launch_mxl<1, 1, 4, 1, 1>(xc, xs, M, w, y, s);
-  return launch_mxl<2, 4, 1, 2, 1>(xc, xs, M, w, y, s);
+  if (M <= 64) return launch_mxl<1, 1, 4, 1, 1, 3>(xc, xs, M, w, y, s);
+  return launch_mxl<2, 4, 1, 2, 1, 3>(xc, xs, M, w, y, s);
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
