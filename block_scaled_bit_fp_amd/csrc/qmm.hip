@@ -363,15 +363,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // One K step: wait for this step's loads (those of the next step stay in
-  // flight), make every wave's loads visible, issue the loads of the step
-  // after next into the stage the previous step used, then run the MFMAs.
+  // flight), make every wave's loads visible, read the first operands, issue
+  // the loads of the step after next into the stage the previous step used,
+  // then run the MFMAs.
   // Past the last step the loads repeat the last step into a stage nobody
   // reads, so every step has the same loads in flight.
   const int nsteps = K / 64;
   auto step = [&](int st, int si, int pi) {
     wait_vmem_le<kStepLoads>();
     __syncthreads();
-    load_step(min(st + 2, nsteps - 1), stage(pi));
     const uint4* cur = stage(si);
     BFrag b[WNT];
     if constexpr (!DENSE) read_b(cur, st, b);
@@ -400,6 +400,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     uint4 a0[WMT], a1[WMT];
     read_a(0, a0);
     read_a(1, a1);
+    // the step's first LDS reads go out before the loads of the step after
+    // next, so their latency overlaps the load issue
+    load_step(min(st + 2, nsteps - 1), stage(pi));
     mma(0, a0);
     read_a(2, a0);
     mma(1, a1);
