@@ -264,6 +264,10 @@ bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_
                 "bsfp_qmm: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only");
   if (M > (1 << 30) || w->rows > (1 << 30))
     return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: M or N beyond 2^30");
+  // every launch shape keeps its grid under 2^32 threads up to 2^33 outputs
+  if ((uint64_t)M * (uint64_t)w->rows > (1ULL << 33))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: M * N = %llu beyond 2^33",
+                (unsigned long long)M * (unsigned long long)w->rows);
   // the GEMM addresses a 256-row activation tile with 32-bit byte offsets
   if (w->cols > (1 << 22))
     return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld beyond 2^22",
@@ -296,6 +300,9 @@ bsfp_status bsfp_qmm_dense(const uint16_t* x, int64_t M, const bsfp_qtensor* w, 
                 (long long)w->cols);
   if (M > (1 << 30) || w->rows > (1 << 30))
     return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: M or N beyond 2^30");
+  if ((uint64_t)M * (uint64_t)w->rows > (1ULL << 33))
+    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: M * N = %llu beyond 2^33",
+                (unsigned long long)M * (unsigned long long)w->rows);
   if (w->cols > (1 << 22))
     return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm_dense: K = %lld beyond 2^22",
                 (long long)w->cols);

@@ -207,7 +207,8 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
  * bsfp_qmm_workspace_bytes(...) bytes (16-byte aligned) and is overwritten.
  * x and y must be 16-byte aligned, w's scales and biases 4-byte aligned.
  * K must be a multiple of 64 and at most
- * 2^22, M and N at most 2^30; BSFP_ACT_SAME needs NVFP4 or MXFP4 weights.
+ * 2^22, M and N at most 2^30 and M * N at most 2^33; BSFP_ACT_SAME needs
+ * NVFP4 or MXFP4 weights.
  * Outside these limits the call returns BSFP_ERR_UNSUPPORTED and launches
  * nothing.
  */

@@ -159,3 +159,22 @@ def test_time_next_launch_set_and_clear(blib):
     assert L.bsfp_time_next_launch(None, None) == 0
     assert L.bsfp_time_next_launch(FAKE, FAKE) == 0
     assert L.bsfp_time_next_launch(None, None) == 0
+
+
+def test_qmm_size_limits(blib):
+    """Shapes beyond the GEMM entry points' limits (M, N <= 2^30, M * N <=
+    2^33, K <= 2^22) are refused before anything is launched."""
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    S = C.c_void_p(FAKE)
+    cases = [((1 << 30) + 1, 4, 64, "2^30"),     # M
+             (4, (1 << 30) + 1, 64, "2^30"),     # N
+             (1 << 20, 1 << 14, 64, "2^33"),     # M * N = 2^34
+             ((1 << 19) + 1, 1 << 14, 64, "2^33"),
+             (4, 4, (1 << 22) + 64, "2^22")]     # K
+    for M, N, K, word in cases:
+        d = desc(blib, rows=N, cols=K)
+        st, msg = status(blib, L.bsfp_qmm(X, M, C.byref(d), 0, None, 0, X, None))
+        assert st == "BSFP_ERR_UNSUPPORTED" and word in msg, (M, N, K, msg)
+        st, msg = status(blib, L.bsfp_qmm_dense(X, M, C.byref(d), S, 1 << 62, X, None))
+        assert st == "BSFP_ERR_UNSUPPORTED" and word in msg, (M, N, K, msg)
