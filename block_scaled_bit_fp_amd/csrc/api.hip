@@ -71,6 +71,10 @@ bsfp_status check_qtensor(const bsfp_qtensor* q, const char* fn) {
   if (q->cols % q->group_size)
     return fail(BSFP_ERR_ARG, "%s: cols %lld is not a multiple of the %s group size %d", fn,
                 (long long)q->cols, mode_name(q->mode), (int)q->group_size);
+  // element counts (rows * cols) are formed in int64 from here on
+  if (q->rows > 0 && q->cols > 0 && q->rows > (int64_t(1) << 40) / q->cols)
+    return fail(BSFP_ERR_UNSUPPORTED, "%s: [%lld, %lld] holds more than 2^40 elements", fn,
+                (long long)q->rows, (long long)q->cols);
   if (q->rows > 0 && q->cols > 0) {
     if (!q->codes || !q->scales)
       return fail(BSFP_ERR_ARG, "%s: null codes or scales", fn);

@@ -107,7 +107,7 @@ typedef struct {
     int32_t mode;          /* bsfp_mode */
     int32_t bits;          /* 4 */
     int32_t group_size;    /* 16 NVFP4, 32 MXFP4, 64 AFFINE */
-    int64_t rows, cols;    /* cols % group_size == 0 */
+    int64_t rows, cols;    /* cols % group_size == 0; rows * cols <= 2^40 */
     uint32_t* codes;       /* [rows, cols/8] */
     void* scales;          /* NVFP4/MXFP4 uint8, AFFINE bf16: [rows, cols/group] */
     uint16_t* biases;      /* AFFINE bf16 [rows, cols/group]; NULL otherwise */

@@ -178,3 +178,17 @@ def test_qmm_size_limits(blib):
         assert st == "BSFP_ERR_UNSUPPORTED" and word in msg, (M, N, K, msg)
         st, msg = status(blib, L.bsfp_qmm_dense(X, M, C.byref(d), S, 1 << 62, X, None))
         assert st == "BSFP_ERR_UNSUPPORTED" and word in msg, (M, N, K, msg)
+
+
+def test_element_count_limit(blib):
+    """A descriptor of more than 2^40 elements is refused by every entry
+    point before rows * cols is used."""
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    for rows, cols in (((1 << 40) // 64 + 1, 64), (1 << 62, 1 << 40)):
+        d = desc(blib, rows=rows, cols=cols)
+        for rc in (L.bsfp_quantize(X, C.byref(d), 0, None), L.bsfp_dequantize(C.byref(d), X, None),
+                   L.bsfp_qmv(X, 1, C.byref(d), X, None),
+                   L.bsfp_qmm(X, 4, C.byref(d), 0, None, 0, X, None)):
+            st, msg = status(blib, rc)
+            assert st == "BSFP_ERR_UNSUPPORTED" and "2^40" in msg, msg
