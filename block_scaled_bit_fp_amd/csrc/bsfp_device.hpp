@@ -335,4 +335,43 @@ __device__ __forceinline__ uint4 buffer_load_u128(rsrc_t r, int voff, int soff) 
 // including the direct-to-LDS ones the compiler does not track.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer straight into LDS: M0 holds the
+// wave-uniform LDS byte offset and lane i lands at M0 + 16 i.  Written as
+// inline assembly on purpose: the compiler does not track it, so it adds no
+// waits of its own before LDS reads of other buffers (it cannot tell the
+// buffers apart and would otherwise hold every read behind every such load);
+// the kernel waits for these loads itself, with an explicit vmcnt before it
+// reads the buffer (and a barrier when other waves read it).
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff, int soff) {
+  typedef __attribute__((address_space(3))) uint4 lds_u4;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u4*)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave still in
+// flight (loads complete in issue order), the direct-to-LDS ones included.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 4 bytes per lane from a buffer straight into LDS (lane i lands at M0 + 4 i),
+// untracked by the compiler like buffer_load_lds16.
+__device__ __forceinline__ void buffer_load_lds4(rsrc_t r, void* lds, int voff, int soff) {
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u32*)lds);
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
+               : "memory");
+}
+
 }  // namespace bsfp

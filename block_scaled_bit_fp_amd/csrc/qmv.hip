@@ -369,12 +369,18 @@ __device__ __forceinline__ void stage_x_store(int M, int NJ, const uint4 (&xr)[X
   }
 }
 
-// Bytes of the per-wave scale staging area of one block of 2R rows
-// (scales, then affine biases).
+// Scale bytes of one block of 2R rows (the affine biases are as many again).
 template <int MODE>
 int block_scale_bytes(int R, int K) {
-  const int srb = (K / fmt_group(MODE)) * fmt_sbytes(MODE);
-  return 2 * R * srb * (fmt_affine(MODE) ? 2 : 1);
+  return 2 * R * (K / fmt_group(MODE)) * fmt_sbytes(MODE);
+}
+
+// LDS bytes of one wave's scale staging: two block buffers (alternate
+// blocks), each of whole 1 KB load windows of scales, then as many of biases.
+template <int MODE>
+int slds_wave_bytes(int R, int K) {
+  const int win = (block_scale_bytes<MODE>(R, K) + 1023) >> 10;
+  return 2 * win * 1024 * (fmt_affine(MODE) ? 2 : 1);
 }
 
 // MAXM: compile-time bound on M.  R: rows per team per block.
@@ -382,13 +388,16 @@ int block_scale_bytes(int R, int K) {
 //   have no chunk in the last step; their scale and bias are forced to zero
 //   (x is zero there already) so a NaN or Inf scale of the next row cannot
 //   leak in.
-// SLDS: the block's scales (2R rows, contiguous) are fetched with 16-byte
-//   loads when its first step is fetched, written to a per-wave LDS area when
-//   that step is consumed, and read from there per chunk -- instead of one
-//   1- or 2-byte load per chunk.  Needs a whole number of 16-byte pieces per
-//   row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and PJ <= NJ,
-//   so that the next
-//   block's scales are fetched only after this block's are in LDS.
+// SLDS: the block's scales (2R rows, contiguous) go straight from memory
+//   into one of the wave's two LDS block buffers (16 bytes per lane and
+//   load, issued just before the codes of the block's first step) and are
+//   read from there per chunk -- instead of one 1- or 2-byte load per chunk.
+//   Consecutive blocks of a wave alternate buffers, so a block's scales land
+//   while the previous block still reads its own.  The loads are not tracked
+//   by the compiler: the first step of a block waits for them explicitly,
+//   which costs nothing, since loads complete in issue order and that step's
+//   codes were issued after them.  Needs a whole number of 16-byte pieces per
+//   row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and PJ <= NJ.
 // QX (qq decode): x is quantized with the weights' format while it is
 // staged and the products run on its exact dequantization; for NVFP4 with
 // qx_amax set, every workgroup takes the global activation scale
@@ -409,6 +418,7 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   constexpr int BITS = fmt_bits(MODE);
   constexpr int CB = 4 * BITS;   // code bytes of a 32-element chunk
   constexpr int PJ = kRing / R;  // steps in flight
+  constexpr int LPS = R * (BITS == 8 ? 2 : 1);  // code loads per step
   constexpr int gs = fmt_group(MODE);
   constexpr int sbytes = fmt_sbytes(MODE);
   constexpr int sstep = 32 * 32 / gs * sbytes;  // scale bytes of one step (32 chunks)
@@ -431,11 +441,14 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   const int steps = passes * NJ;
   float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
 
-  // this wave's scale area (SLDS): [2R rows][srb] scales, then the biases
+  // this wave's scale areas (SLDS): two block buffers, each nsl KB of
+  // [2R rows][srb] scales, then nsl KB of biases
   const int sarea = 2 * R * srb;
-  uint8_t* sl = reinterpret_cast<uint8_t*>(
-      smem + (M * NJ * (AFF ? 136 : 128))) + wave_in_wg * (AFF ? 2 : 1) * sarea;
   const int nsl = (sarea + 1023) >> 10;  // 16-byte scale loads per lane and array
+  const int sbuf = nsl * 1024;           // bytes of one array in one buffer
+  const int spar = (AFF ? 2 : 1) * sbuf;  // bytes of one block buffer
+  uint8_t* sl = reinterpret_cast<uint8_t*>(smem + (M * NJ * (AFF ? 136 : 128))) +
+                wave_in_wg * 2 * spar;
 
   int vc[R], vs[R];
 #pragma unroll
@@ -459,15 +472,19 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
       rbs = make_rsrc(reinterpret_cast<const uint8_t*>(biases) + row0 * srb, rows * srb);
   };
   constexpr int SL = (MODE == BSFP_NVFP4) ? 4 : 2;
-  uint4 sreg[SLDS ? SL : 1], breg[SLDS && AFF ? SL : 1];
-  auto fetch = [&](Chunk (&dst)[R], int j) {
+  // fetch step j of the current block; `real` is false for the refills past
+  // the wave's last step, `par` is the block's buffer
+  auto fetch = [&](Chunk (&dst)[R], int j, bool real, int par) {
     if constexpr (SLDS) {
-      if (j == 0) {  // the block's scales, 16 bytes per lane and load
+      if (j == 0 && real) {  // the block's scales, straight into its LDS buffer
+        uint8_t* b = sl + par * spar;
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
           if (i < nsl) {
-            sreg[i] = buffer_load_u128(rs, 16 * lane, i * 1024);
-            if constexpr (AFF) breg[i] = buffer_load_u128(rbs, 16 * lane, i * 1024);
+            buffer_load_lds16(rs, reinterpret_cast<uint4*>(b + i * 1024), 16 * lane + i * 1024, 0);
+            if constexpr (AFF)
+              buffer_load_lds16(rbs, reinterpret_cast<uint4*>(b + sbuf + i * 1024),
+                                16 * lane + i * 1024, 0);
           }
         }
       }
@@ -501,15 +518,23 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   stage_x_load(x, M, K, NJ, xr);
   Chunk ring[PJ][R];
   int pf = 0, jf = 0;  // next step to fetch
+  // The first PJ steps are fetched by every wave (a wave with no rows reads
+  // through empty descriptors, which returns zeros without touching memory),
+  // so the compiler sees a fixed number of loads after the x loads and the
+  // x staging below waits for the x loads alone.
   if (steps > 0) {
     set_block(0);
+  } else {
+    rc = make_rsrc(codes, 0);
+    rs = make_rsrc(scales, 0);
+    if constexpr (AFF) rbs = make_rsrc(biases, 0);
+  }
 #pragma unroll
-    for (int u = 0; u < PJ; ++u) {
-      fetch(ring[u], pf < passes ? jf : NJ - 1);
-      if (pf < passes && ++jf == NJ) {
-        jf = 0;
-        if (++pf < passes) set_block(pf);
-      }
+  for (int u = 0; u < PJ; ++u) {
+    fetch(ring[u], pf < passes ? jf : NJ - 1, pf < passes, pf & 1);
+    if (pf < passes && ++jf == NJ) {
+      jf = 0;
+      if (++pf < passes) set_block(pf);
     }
   }
   float gq = 1.0f;
@@ -538,7 +563,10 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   }
   stage_x_store<AFF, AFF && BITS == 4, fast_xu<MODE, MAXM>(), QX ? MODE : -1>(M, NJ, xr, xp, xs, gq);
   __syncthreads();
-  if (steps == 0) return;
+  if (steps == 0) {
+    wait_vmem();  // the empty refills have returned
+    return;
+  }
 
   int pc = 0, jc = 0;  // next step to consume
   for (int s0 = 0; s0 < steps; s0 += PJ) {
@@ -546,28 +574,19 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
     for (int u = 0; u < PJ; ++u) {
       if (s0 + u < steps) {
         if constexpr (SLDS) {
-          if (jc == 0) {  // this block's scales into the wave's LDS area
-#pragma unroll
-            for (int i = 0; i < SL; ++i) {
-              if (i < nsl) {
-                if (16 * (lane + 64 * i) < sarea) {
-                  *reinterpret_cast<uint4*>(sl + 16 * (lane + 64 * i)) = sreg[i];
-                  if constexpr (AFF)
-                    *reinterpret_cast<uint4*>(sl + sarea + 16 * (lane + 64 * i)) = breg[i];
-                }
-              }
-            }
-          }
+          // this block's scales were issued before the codes of this step:
+          // once at most PJ steps of code loads are in flight, they are in LDS
+          if (jc == 0) wait_vmem_le<PJ * LPS>();
         }
         const bool valid = !RAGGED || (32 * jc + lt < cpr);
         uint32_t sv[R], bv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if constexpr (SLDS) {
-            const uint8_t* sp = sl + vs[r] + jc * sstep;
+            const uint8_t* sp = sl + (pc & 1) * spar + vs[r] + jc * sstep;
             if constexpr (AFF) {
               sv[r] = *reinterpret_cast<const uint16_t*>(sp);
-              bv[r] = *reinterpret_cast<const uint16_t*>(sp + sarea);
+              bv[r] = *reinterpret_cast<const uint16_t*>(sp + sbuf);
             } else if constexpr (MX) {
               sv[r] = *sp;
             } else {
@@ -696,7 +715,7 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
       }
       // refill this slot with step s0 + u + PJ (past the end: reload the last
       // step, whose data is never consumed)
-      fetch(ring[u], pf < passes ? jf : NJ - 1);
+      fetch(ring[u], pf < passes ? jf : NJ - 1, pf < passes, pf & 1);
       if (pf < passes && ++jf == NJ) {
         jf = 0;
         if (++pf < passes) set_block(pf);
@@ -755,7 +774,7 @@ FastShape fast_shape(int M, int K, int NJ, int64_t N) {
   const int wpg = (int)std::min<int64_t>(
       kMaxW, std::max<int64_t>(min_wpg, (nblocks + grid * passes - 1) / (grid * passes)));
   size_t lds = fast_lds_bytes<MODE>(M, NJ) +
-               (SLDS ? (size_t)wpg * block_scale_bytes<MODE>(R, K) : 0);
+               (SLDS ? (size_t)wpg * slds_wave_bytes<MODE>(R, K) : 0);
   const size_t half = (size_t)device_max_lds() / 2 + 16;
   if (kPerCu == 1 && grid == cus && wpg <= 8 && lds < half) lds = half;
   return FastShape{(int)grid, wpg, lds};
@@ -802,7 +821,7 @@ bool fast_ok(int M, int NJ) {
 template <int MODE, int R>
 bool slds_ok(int K, int NJ, int M, int64_t N) {
   const int cpr = K / 32;
-  const int sarea = block_scale_bytes<MODE>(R, K) / (fmt_affine(MODE) ? 2 : 1);
+  const int sarea = block_scale_bytes<MODE>(R, K);
   const int srb = sarea / (2 * R);
   if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || kRing / R > NJ) return false;
   return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
