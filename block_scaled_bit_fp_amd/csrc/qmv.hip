@@ -280,9 +280,19 @@ __global__ __launch_bounds__(kThreads) void qmv_nvfp4_words_kernel(
 // LDS once and used for R rows.  All addresses are per-lane constants plus
 // wave-uniform offsets (raw buffer loads: descriptor at the block's first row,
 // 32-bit lane offset, scalar step offset); rows past N fall outside the
-// descriptor and read as zeros.  kRing chunk loads per lane stay in flight,
-// and the pipeline runs across row blocks.
-constexpr int kRing = 8;
+// descriptor and read as zeros.  A few steps of chunk loads per lane stay in
+// flight (steps_in_flight), and the pipeline runs across row blocks.
+//
+// Steps in flight per wave: 3 with one row per team, 2 with more (4 and 8
+// chunk loads per lane).  Deeper rings measured slower: on the affine
+// [5120, 25600] decode shape (one row per team) 20.3 us with 8 loads per lane
+// and 22.3 us with 16, against 18.9 us with 3; on [25600, 5120] (two rows per
+// team) 16.8 us with 8 against 16.2 us with 4.  The whole chip already keeps
+// every row of such a matrix in flight at once.
+template <int R>
+constexpr int steps_in_flight() {
+  return R == 1 ? 3 : 2;
+}
 
 struct Chunk {
   uint4 w;     // 32 codes (4-bit), or the first 16 of them (8-bit)
@@ -417,7 +427,7 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   constexpr bool MX = (MODE == FMT_MXFP4 || MODE == FMT_MXFP8);  // one E8M0 byte per chunk
   constexpr int BITS = fmt_bits(MODE);
   constexpr int CB = 4 * BITS;   // code bytes of a 32-element chunk
-  constexpr int PJ = kRing / R;  // steps in flight
+  constexpr int PJ = steps_in_flight<R>();
   constexpr int LPS = R * (BITS == 8 ? 2 : 1);  // code loads per step
   constexpr int gs = fmt_group(MODE);
   constexpr int sbytes = fmt_sbytes(MODE);
@@ -823,7 +833,7 @@ bool slds_ok(int K, int NJ, int M, int64_t N) {
   const int cpr = K / 32;
   const int sarea = block_scale_bytes<MODE>(R, K);
   const int srb = sarea / (2 * R);
-  if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || kRing / R > NJ) return false;
+  if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || steps_in_flight<R>() > NJ) return false;
   return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
 }
 
