@@ -36,8 +36,9 @@ The JSON line reports the headline metric: `value` is the sustained qmv GB/s
 of the 64-layer sweep (algorithmic bytes: packed codes + scales + biases +
 x + y per matrix); `qmm_tflops` the NVFP4 qqmm TFLOP/s at M = 2048 per whole
 call (activation amax and quantize, then the GEMM).  `roofline` is for the qmv
-kernel (HBM), `roofline_qmm` for the qqmm GEMM kernel alone (fp16 MFMA), both
-over kernel durations taken with HIP events attached to the launches.
+kernel (HBM), over the mean launch duration of the sweep's back-to-back GEMV
+launches (HIP events on their stream); `roofline_qmm` for the qqmm GEMM kernel
+alone (fp16 MFMA), over HIP events attached to its first and last launch.
 `cpu_baseline` times the CPU oracle on a bounded sample.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -171,22 +172,14 @@ def main():
         b.quantize(W_mx_bf, b.MXFP4, out=q_mx_out)
         b.quantize(W_small, b.AFFINE, out=q_small_out)
 
-    # Kernel-level timing of the sweep's GEMV: every 16th launch of a timed
-    # sweep carries a pair of HIP events that record that kernel's own start
-    # and end (bsfp_time_next_launch).  A timed launch costs a few us of extra
-    # queue latency, so only a sample is timed; 16 = 1 (mod 3) cycles the
-    # sample through the gate, up and down matrices.
-    SAMPLE = 16
-    hip = HipEvents((len(sweep) // SAMPLE + 2) * args.steps * 2)
+    # The sweep's GEMV launches run back to back on one stream, between one
+    # pair of HIP events: the mean launch duration is the sweep's time over
+    # its launches (the short gaps between launches included).
+    hip = HipEvents(4 * args.steps + 4)
     recording = [False]
-    launch_ev = []
 
-    def st_qmv_sweep(record=False):
-        for i, (x, q, y) in enumerate(sweep):
-            if record and i % SAMPLE == 0:
-                e0, e1 = hip.take(), hip.take()
-                b.time_next_launch(e0, e1)
-                launch_ev.append((q.rows, e0, e1))
+    def st_qmv_sweep():
+        for x, q, y in sweep:
             b.qmv(x, q, out=y)
 
     def st_qmv_fp4():
@@ -293,7 +286,7 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn(record=True) if n == "qmv_sweep" else fn()
+                fn()
                 e1.record(stream)
                 ev[n].append((e0, e1))
             else:
@@ -330,11 +323,7 @@ def main():
         out["value"] = round(gbs, 1)
         out["qmv_sweep_gbs"] = round(gbs, 1)
         per_launch = sweep_bytes / len(sweep)
-        durs = {}
-        for rows, e0, e1 in launch_ev:
-            durs.setdefault(rows, []).append(hip.elapsed_ms(e0, e1))
-        all_ms = [d for v in durs.values() for d in v]
-        launch_ms = float(np.mean(all_ms))
+        launch_ms = ms["qmv_sweep"] / len(sweep)
         kgbs = per_launch / (launch_ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
@@ -342,14 +331,12 @@ def main():
                            "kernel": "qmv_fast_kernel<affine, M=1>",
                            "bytes_per_launch": int(per_launch),
                            "launch_us": round(launch_ms * 1e3, 3),
-                           "launch_us_by_shape": {
-                               ("[25600,5120]" if r == INTER else "[5120,25600]"):
-                                   round(float(np.mean(v)) * 1e3, 3) for r, v in durs.items()},
-                           "timed_launches": len(all_ms),
-                           "note": "algorithmic bytes of one launch / mean kernel duration "
-                                   "of every 16th launch of the timed sweeps (HIP start/stop "
-                                   "events attached to the GEMV launch); value is the whole "
-                                   "sweep including the gaps between launches"}
+                           "launches_per_sweep": len(sweep),
+                           "note": "algorithmic bytes of one launch / mean launch duration: "
+                                   "HIP events on the GEMV's stream around the sweep's "
+                                   "back-to-back launches (median over the timed steps) "
+                                   "divided by their number, so the short gaps between "
+                                   "launches count as kernel time"}
     if "qqmm" in ms:
         flop = 2.0 * 2048 * INTER * HIDDEN
         tfs = flop / (ms["qqmm"] * 1e-3) / 1e12
