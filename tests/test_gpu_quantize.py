@@ -141,6 +141,24 @@ def test_amax_matches_oracle(oracle_mod, bsfp):
     assert bsfp.amax(torch.zeros(0, dtype=torch.bfloat16, device="cuda")).item() == 0.0
 
 
+@pytest.mark.gpu
+def test_amax_planted_maximum_anywhere(oracle_mod, bsfp):
+    """One element of magnitude 7.5 (negative) among N(0,1) values, planted at
+    the start, the middle, the last whole 8-element word, the n % 8 tail and
+    the end; amax must be exactly 7.5 wherever it sits, also on repeated calls
+    into a buffer that already holds a larger stale value."""
+    n = 4096 * 5120 + 5
+    base = S.generic((n,), 1.0, seed=77)
+    base = (base & 0x8000) | np.minimum(base & 0x7FFF, 0x4060)  # |x| <= 3.5 (bf16 bits)
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    for pos in (0, n // 2 + 3, (n // 8) * 8 - 1, n - 3, n - 1):
+        x = base.copy()
+        x[pos] = 0xC0F0  # bf16 -7.5
+        out.fill_(1000.0)
+        got = bsfp.amax(to_dev(x), out=out).item()
+        assert got == 7.5 == oracle_mod.amax(x), pos
+
+
 def test_quantize_is_deterministic(bsfp):
     x = to_dev(S.nvfp4_activations(512, 5120, seed=9))
     a = bsfp.quantize(x, 2)
