@@ -13,7 +13,11 @@ already resident in HBM:
   qmv_sweep   affine g64 decode GEMV over 64 layers x {gate, up, down}
               ([25600,5120], [25600,5120], [5120,25600]): 192 distinct matrices,
               14.17 GB of packed weights (more than the 256 MB Infinity Cache)
-  qmv_fp4     MXFP4 qmv W[5760,2880] at M = 1 and 8, NVFP4 qmv [25600,5120] M=1
+  qmv_mx1 / qmv_mx8   MXFP4 qmv W[5760,2880] at M = 1 and 8: a burst of 32
+              calls over 32 distinct weight copies (282 MB, more than the
+              Infinity Cache), reported per call (`qmv_fp4_gbs`)
+  qmv_nv1     NVFP4 qmv W[25600,5120] at M = 1: a burst of 8 calls over 4
+              distinct matrices, reported per call (`qmv_fp4_gbs`)
   qqmm        NVFP4 prefill X[2048,5120] . W[25600,5120]^T (x quantized on the
               fly, alpha = g_x g_w), the headline GEMM
   qqmm_1134 / qqmm_4096   the same GEMM at M = 1134 and 4096
@@ -182,10 +186,6 @@ def main():
         for x, q, y in sweep:
             b.qmv(x, q, out=y)
 
-    def st_qmv_fp4():
-        b.qmv(x_mx[1], q_mx, out=y_mx[1])
-        b.qmv(x_mx[8], q_mx, out=y_mx[8])
-        b.qmv(x_nv1, q_pf, out=y_nv1)
 
     # The M = 2048 qq stage also times its GEMM launches alone: a pair of HIP
     # events that the library attaches to the first and last GEMM launch of
@@ -210,7 +210,7 @@ def main():
     # kernels' own streaming rate, not one call's host latency; stage times
     # of these stages are per call.
     BURST, NDIST = 8, 4
-    per_call = {"qq_decode"}
+    per_call = {"qq_decode": BURST}  # stage -> calls per timed burst
     q_dec = [q_pf] + [b.quantize(S.torch_normal_bf16((INTER, HIDDEN), 0.02, 910 + i, dev),
                                  b.NVFP4) for i in range(NDIST - 1)]
 
@@ -220,6 +220,25 @@ def main():
 
     def mx(M):
         return lambda: b.qmm(x_mx[M], q_mx, act="same", workspace=ws_mx[M], out=y_mx[M])
+
+    # decode GEMV on 4-bit float weights: MXFP4 W[5760,2880] at M = 1 and 8
+    # over MXROT distinct copies, NVFP4 W[25600,5120] at M = 1 over the qq
+    # decode stage's NDIST matrices
+    MXROT = 32
+    q_mx_rot = [q_mx] + [b.quantize(S.torch_normal_bf16((5760, 2880), 0.02, 950 + i, dev),
+                                    b.MXFP4) for i in range(MXROT - 1)]
+
+    def qmv_mx(M):
+        def run():
+            for q in q_mx_rot:
+                b.qmv(x_mx[M], q, out=y_mx[M])
+        return run
+
+    def st_qmv_nv1():
+        for i in range(BURST):
+            b.qmv(x_nv1, q_dec[i % NDIST], out=y_nv1)
+
+    per_call.update({"qmv_mx1": MXROT, "qmv_mx8": MXROT, "qmv_nv1": BURST})
 
     def st_qmm_affine():
         b.qmm(X_aff, q_up0, act="bf16", out=Y_aff)
@@ -235,7 +254,7 @@ def main():
             wb = S.torch_normal_bf16((INTER, HIDDEN), 0.02, 900 + 16 * i + j, dev)
             q_var[name].append(b.quantize(wb, mode, bits=nb, group=G))
             del wb
-        per_call.add(f"qmv_{name}")
+        per_call[f"qmv_{name}"] = BURST
 
     def var_bytes(name):
         mode, nb, G = VARIANTS[name]
@@ -260,7 +279,8 @@ def main():
 
     stages = [("act_quant", st_act_quant), ("act_quant_sr", st_act_quant_sr),
               ("dequant", st_dequant), ("w_quant", st_w_quant),
-              ("qmv_sweep", st_qmv_sweep), ("qmv_fp4", st_qmv_fp4), ("qqmm", qq(2048)),
+              ("qmv_sweep", st_qmv_sweep), ("qmv_mx1", qmv_mx(1)), ("qmv_mx8", qmv_mx(8)),
+              ("qmv_nv1", st_qmv_nv1), ("qqmm", qq(2048)),
               ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qq_decode", st_qq_decode),
               ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)),
               ("qmm_affine", st_qmm_affine)]
@@ -302,7 +322,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    ms = {n: float(np.median([a.elapsed_time(c) for a, c in ev[n]])) / (BURST if n in per_call else 1)
+    ms = {n: float(np.median([a.elapsed_time(c) for a, c in ev[n]])) / per_call.get(n, 1)
           for n in names}
     log("[bench] stage medians (ms): " + ", ".join(f"{n}={ms[n]:.3f}" for n in names))
 
@@ -374,6 +394,14 @@ def main():
                              "dense_over_fused": round(ms[f"wonly_{M}"] / ms[f"dense_{M}"], 3)}
     if cross:
         out["dense_crossover"] = cross
+    fp4 = {}
+    for key, stage, nbytes in (("mxfp4_m1", "qmv_mx1", fp4_bytes(5760, 2880, 32, 1)),
+                               ("mxfp4_m8", "qmv_mx8", fp4_bytes(5760, 2880, 32, 8)),
+                               ("nvfp4_m1", "qmv_nv1", fp4_bytes(INTER, HIDDEN, 16, 1))):
+        if stage in ms:
+            fp4[key] = round(nbytes / (ms[stage] * 1e-3) / 1e9, 1)
+    if fp4:
+        out["qmv_fp4_gbs"] = fp4
     if "qq_decode" in ms:
         out["qq_decode_gbs"] = round(fp4_bytes(INTER, HIDDEN, 16) / (ms["qq_decode"] * 1e-3) / 1e9, 1)
     if "qmm_mx32" in ms:  # HBM-bound size: weight + activation bytes per call
