@@ -50,6 +50,16 @@ def test_qmv_ragged(oracle_mod, bsfp, mode, M, N, K):
     check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_qmv_many_blocks_per_wave(oracle_mod, bsfp, mode):
+    """A tall matrix (N = 40001, K = 2048): with two rows per team every wave
+    walks three or more row blocks, so the staged block scales cycle through
+    both of a wave's LDS buffers more than once; the last block is one row."""
+    x = S.generic((1, 2048), 1.0, seed=410)
+    w = S.generic((40001, 2048), 0.02, seed=411 + mode)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
 def test_nvfp4_k_not_multiple_of_32(oracle_mod, bsfp):
     for M in (1, 4):
         for K in (16, 48, 16 * 33):
