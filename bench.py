@@ -91,7 +91,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by weight rows; see DESIGN.md)", file=sys.stderr)
+              "(the path shards W by output rows, and one GPU's share is the same "
+              "kernel at a smaller N)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
