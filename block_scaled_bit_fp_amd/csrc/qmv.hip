@@ -404,10 +404,13 @@ int slds_wave_bytes(int R, int K) {
 //   read from there per chunk -- instead of one 1- or 2-byte load per chunk.
 //   Consecutive blocks of a wave alternate buffers, so a block's scales land
 //   while the previous block still reads its own.  The loads are not tracked
-//   by the compiler: the first step of a block waits for them explicitly,
-//   which costs nothing, since loads complete in issue order and that step's
-//   codes were issued after them.  Needs a whole number of 16-byte pieces per
-//   row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and PJ <= NJ.
+//   by the compiler: the first step of a block waits for them explicitly.
+//   Memory operations complete in issue order and that step's codes were
+//   issued after them, so the wait (at most PJ steps of loads in flight) is
+//   one the step's own code loads need anyway; output stores issued since
+//   only make it slightly stricter.  Needs a whole number of 16-byte pieces
+//   per row, at most SL loads per lane (4 for NVFP4, 2 otherwise), and
+//   PJ <= NJ.
 // QX (qq decode): x is quantized with the weights' format while it is
 // staged and the products run on its exact dequantization; for NVFP4 with
 // qx_amax set, every workgroup takes the global activation scale
