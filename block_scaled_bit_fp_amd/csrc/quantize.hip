@@ -22,6 +22,8 @@
 //          exponent); S = e + 127; code = E2M1(x * 2^-e).
 //   AFFINE s = bf16((max - min)/15), b = bf16(min) = min,
 //          q = clamp(rint((x - b) * (1/s)), 0, 15), s == 0 -> q = 0.
+#include <algorithm>
+
 #include "bsfp_device.hpp"
 #include "bsfp_internal.hpp"
 
