@@ -295,17 +295,17 @@ def main():
     def dense(M):
         return lambda: b.qmm_dense(X_pf[M], q_pf, scratch=dense_scratch, out=Y_pf[M])
 
+    # quantize stages, then every decode GEMV, then the prefill GEMMs
     stages = [("act_quant", st_act_quant), ("act_quant_warm", st_act_quant_warm),
               ("act_quant_sr", st_act_quant_sr),
               ("dequant", st_dequant), ("w_quant", st_w_quant),
               ("qmv_sweep", st_qmv_sweep), ("qmv_mx1", qmv_mx(1)), ("qmv_mx8", qmv_mx(8)),
-              ("qmv_nv1", st_qmv_nv1), ("qqmm", qq(2048)),
-              ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)), ("qq_decode", st_qq_decode),
-              ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)),
-              ("qmm_affine", st_qmm_affine)]
+              ("qmv_nv1", st_qmv_nv1), ("qq_decode", st_qq_decode)]
+    stages += [(f"qmv_{name}", qmv_var(name)) for name in VARIANTS]
+    stages += [("qqmm", qq(2048)), ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)),
+               ("qmm_mx32", mx(32)), ("qmm_mx512", mx(512)), ("qmm_affine", st_qmm_affine)]
     for M in (1134, 2048, 4096):
         stages += [(f"wonly_{M}", wonly(M)), (f"dense_{M}", dense(M))]
-    stages += [(f"qmv_{name}", qmv_var(name)) for name in VARIANTS]
     if args.only:
         keep = set(args.only.split(","))
         stages = [s for s in stages if s[0] in keep]
