@@ -197,8 +197,9 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
  *     g_x * g_w for NVFP4 with a global scale on W (g_x = amax_x/2688,
  *     computed here), else 1.  The pages' alpha = amax_x*amax_w/(448*6)^2
  *     (create_nvfp4_scalars) is the same quantity up to fp32 rounding.
- *     MXFP4 runs on the gfx950 scaled f8f6f4 MFMA; NVFP4 and AFFINE on bf16
- *     MFMA with both operands dequantized exactly.  For M <= 8 (decode) the
+ *     MXFP4 runs on the gfx950 scaled f8f6f4 MFMA; NVFP4 on fp16 MFMA with
+ *     both operands dequantized exactly (E2M1 * E4M3 has at most 6
+ *     significant bits, so fp16 holds it).  For M <= 8 (decode) the
  *     same product runs as the GEMV of bsfp_qmv on q(x) dequantized exactly
  *     to bf16, with alpha applied the same way (the M = 1 branch of
  *     QQMatmul, qqmm.cpp, with the global scale of w kept); when x is at
