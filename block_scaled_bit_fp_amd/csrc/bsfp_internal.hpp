@@ -53,6 +53,13 @@ hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words,
 hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
                                               const float* g_src, int g_src_is_amax,
                                               float* g_out, hipStream_t s);
+// amax of x (as per-workgroup partial maxima in parts[kAmaxParts]) and the
+// fp16 quantize-dequantize (launch_quantize_dequant_nvfp4_f16) with g = amax/2688 taken from the partials:
+// two launches, no initialised memory, no atomics.  *amax_out and *g_out
+// receive the tensor amax and g.  n % 8 == 0.
+constexpr int kAmaxParts = 256;
+hipError_t launch_amax_qdq_nvfp4_f16(const uint16_t* x, int64_t n, void* xhat, float* parts,
+                                     float* amax_out, float* g_out, hipStream_t s);
 // MXFP4 quantize, then exact dequantization to bf16.
 hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
                                               hipStream_t s);

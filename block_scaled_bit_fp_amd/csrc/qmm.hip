@@ -814,15 +814,18 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 // Workspace for the qq paths:
-//   NVFP4: [amax f32, g_x f32] (256 B) + xhat fp16 [M, K]
+//   NVFP4: [amax f32, g_x f32] (256 B), the partial maxima of |x|
+//          (kAmaxParts floats), then xhat fp16 [M, K] (GEMM path); the
+//          decode path puts xhat bf16 [M, K] at byte 256 instead
 //   MXFP4: x codes uint32 [M, K/8] + x scales uint8 [M, K/32]
 // Rows of x up to which the qq product runs as a GEMV on the exactly
 // dequantized x (the decode path) instead of a GEMM.
 constexpr int64_t kQqDecodeRows = 8;
+constexpr size_t kNvWsHead = 256 + kAmaxParts * sizeof(float);
 
 size_t qmm_workspace_bytes(int mode, int64_t M, int64_t K, int act) {
   if (act != BSFP_ACT_SAME) return 0;
-  if (mode == BSFP_NVFP4) return 256 + align256((size_t)M * K * 2);
+  if (mode == BSFP_NVFP4) return kNvWsHead + align256((size_t)M * K * 2);
   if (mode == BSFP_MXFP4) {
     if (M <= kQqDecodeRows) return align256((size_t)M * K * 2);
     return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
@@ -884,11 +887,11 @@ hipError_t launch_qmm(const uint16_t* x, int64_t M64, const bsfp_qtensor& w, int
   if (w.mode == BSFP_NVFP4) {
     float* amax = reinterpret_cast<float*>(ws);
     float* gx = amax + 1;
-    uint16_t* xhat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + 256);
+    float* parts = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 256);
+    uint16_t* xhat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + kNvWsHead);
     hipError_t e = hipSuccess;
     if (w.global_scale) {  // alpha = g_x * g_w with g_x = amax_x / 2688
-      e = launch_amax(x, n, amax, s);
-      if (e == hipSuccess) e = launch_quantize_dequant_nvfp4_f16(x, n / 8, xhat, amax, 1, gx, s);
+      e = launch_amax_qdq_nvfp4_f16(x, n, xhat, parts, amax, gx, s);
       if (e != hipSuccess) return e;
       return run_dq_m<DEC_NVFP4_F16>(xhat, M, w, gx, w.global_scale, y, s);
     }

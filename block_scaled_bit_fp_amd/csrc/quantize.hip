@@ -44,8 +44,10 @@ __global__ void amax_init_kernel(float* out) { *out = 0.0f; }
 // CU, and a workgroup whose max does not exceed the value already there
 // skips its atomic.
 constexpr int kAmaxThreads = 1024;
-__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x,
-                                                             int64_t n, float* __restrict__ out) {
+
+// max |x| over this workgroup's share of the n values (grid-stride, four
+// 16-byte loads in flight per lane); the result is valid in thread 0.
+__device__ __forceinline__ float workgroup_absmax(const uint16_t* __restrict__ x, int64_t n) {
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int64_t nv = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
@@ -78,14 +80,31 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __re
   __shared__ float part[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = part[0];
+  float r = part[0];
 #pragma unroll
-    for (int w = 1; w < kAmaxThreads / 64; ++w) r = fmaxf(r, part[w]);
+  for (int w = 1; w < kAmaxThreads / 64; ++w) r = fmaxf(r, part[w]);
+  return r;
+}
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t n, float* __restrict__ out) {
+  const float r = workgroup_absmax(x, n);
+  if (threadIdx.x == 0) {
     unsigned int* o = reinterpret_cast<unsigned int*>(out);
     const unsigned int cur = __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__float_as_uint(r) > cur) atomicMax(o, __float_as_uint(r));
   }
+}
+
+// The same maximum as per-workgroup partials: parts[blockIdx.x] = max |x|
+// over the workgroup's share.  Needs no initialised output and no atomics;
+// the consumer takes the max of the gridDim.x partials (max is exact in any
+// order, so the result equals amax_kernel's).
+__global__ __launch_bounds__(kAmaxThreads) void amax_parts_kernel(const uint16_t* __restrict__ x,
+                                                                   int64_t n,
+                                                                   float* __restrict__ parts) {
+  const float r = workgroup_absmax(x, n);
+  if (threadIdx.x == 0) parts[blockIdx.x] = r;
 }
 
 // ------------------------------------------------------------------ NVFP4
@@ -138,12 +157,30 @@ __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
 // bsfp_quantize produces for the same input and global scale.
 //   BF16 = true writes bf16 instead (E2M1 * E4M3 has at most 6 significant
 //   bits, so it is exact in bf16 too): the x of the qq decode GEMV.
+//   parts / nparts (nparts <= kThreads): per-workgroup partial maxima of |x|
+//   from amax_parts_kernel; every workgroup reduces them to the tensor amax
+//   and takes g = amax/2688 (g_src is then ignored), and workgroup 0 stores
+//   amax in *amax_out.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint4* __restrict__ xhat,
-    const float* __restrict__ g_src, int g_src_is_amax, float* __restrict__ g_out) {
+    const float* __restrict__ g_src, int g_src_is_amax, float* __restrict__ g_out,
+    const float* __restrict__ parts, int nparts, float* __restrict__ amax_out) {
   float g = 1.0f;
-  if (g_src) g = g_src_is_amax ? (*g_src / 2688.0f) : *g_src;
+  if (parts) {
+    float a = (int)threadIdx.x < nparts ? parts[threadIdx.x] : 0.0f;
+    a = team_max<64>(a);
+    __shared__ float red[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, red[w]);
+    g = a / 2688.0f;
+    if (amax_out && blockIdx.x == 0 && threadIdx.x == 0) *amax_out = a;
+  } else if (g_src) {
+    g = g_src_is_amax ? (*g_src / 2688.0f) : *g_src;
+  }
   if (g_out && blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
   const float six_g = 6.0f * g;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -458,7 +495,22 @@ hipError_t launch_quantize_dequant_nvfp4_f16(const uint16_t* x, int64_t n_words,
                                              float* g_out, hipStream_t s) {
   hipLaunchKernelGGL(quantize_dequant_nvfp4_kernel<false>, dim3(stream_grid(n_words)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
-                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out);
+                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out,
+                     (const float*)nullptr, 0, (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_qdq_nvfp4_f16(const uint16_t* x, int64_t n, void* xhat, float* parts,
+                                     float* amax_out, float* g_out, hipStream_t s) {
+  const int64_t nv = n >> 3;
+  const int64_t want = (nv / 4 + kAmaxThreads) / kAmaxThreads;  // 4 loads per lane
+  const int grid = (int)std::min<int64_t>(std::max<int64_t>(want, 1),
+                                          std::min(device_cu_count(), kAmaxParts));
+  hipLaunchKernelGGL(amax_parts_kernel, dim3(grid), dim3(kAmaxThreads), 0, s, x, n, parts);
+  hipLaunchKernelGGL(quantize_dequant_nvfp4_kernel<false>, dim3(stream_grid(n / 8)),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n / 8,
+                     reinterpret_cast<uint4*>(xhat), (const float*)nullptr, 0, g_out,
+                     (const float*)parts, grid, amax_out);
   return hipGetLastError();
 }
 
@@ -467,7 +519,8 @@ hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words
                                               float* g_out, hipStream_t s) {
   hipLaunchKernelGGL(quantize_dequant_nvfp4_kernel<true>, dim3(stream_grid(n_words)),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(x), n_words,
-                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out);
+                     reinterpret_cast<uint4*>(xhat), g_src, g_src_is_amax, g_out,
+                     (const float*)nullptr, 0, (float*)nullptr);
   return hipGetLastError();
 }
 
