@@ -440,6 +440,50 @@ def main():
         nbytes = 4096 * HIDDEN * (2 * 2 + 4) + 4096 * HIDDEN // 2 + 4096 * HIDDEN // 16
         out["act_quant_sr_gbs"] = round(nbytes / (ms["act_quant_sr"] * 1e-3) / 1e9, 1)
 
+    # Every hot-path row against the roofline that bounds it: algorithmic bytes
+    # (HBM rows) or 2*M*N*K flops (MFMA rows) over the stage's time per call.
+    # Short stages timed as one call on an idle queue (dequant, w_quant,
+    # qmm_mx32, qmm_mx512) include the host side of the call.
+    def hbm_row(stage, nbytes):
+        if stage in ms:
+            a = nbytes / (ms[stage] * 1e-3) / 1e9
+            return {"stage": stage, "bound": "hbm", "achieved": round(a, 1), "unit": "GB/s",
+                    "peak": HBM_PEAK_GBS, "frac": round(a / HBM_PEAK_GBS, 4)}
+
+    def mfma_row(stage, flop, peak):
+        if stage in ms:
+            a = flop / (ms[stage] * 1e-3) / 1e12
+            return {"stage": stage, "bound": "mfma", "achieved": round(a, 1), "unit": "TFLOP/s",
+                    "peak": peak, "frac": round(a / peak, 4)}
+
+    NX = 4096 * HIDDEN
+    rows = {
+        "a1+a2 NVFP4 activation amax + quantize [4096,5120], cold":
+            hbm_row("act_quant", NX * 2 * 2 + NX // 2 + NX // 16),
+        "a3+a4 MXFP4 quantize W[5760,2880] + affine quantize W[1024,512]":
+            hbm_row("w_quant", 5760 * 2880 * 2 + 5760 * 2880 // 2 + 5760 * 90
+                    + 1024 * 512 * 2 + 1024 * 512 // 2 + 2 * 2 * 1024 * 8),
+        "a5 NVFP4 dequantize [4096,5120]": hbm_row("dequant", NX // 2 + NX // 16 + NX * 2),
+        "a6 affine qmv sweep": hbm_row("qmv_sweep", sweep_bytes),
+        "a7 NVFP4 qmv [25600,5120] M=1": hbm_row("qmv_nv1", fp4_bytes(INTER, HIDDEN, 16, 1)),
+        "a7 MXFP4 qmv [5760,2880] M=1": hbm_row("qmv_mx1", fp4_bytes(5760, 2880, 32, 1)),
+        "a7 MXFP4 qmv [5760,2880] M=8": hbm_row("qmv_mx8", fp4_bytes(5760, 2880, 32, 8)),
+        "a8+a9+a12 NVFP4 qqmm M=2048, whole call":
+            mfma_row("qqmm", 2.0 * 2048 * INTER * HIDDEN, MFMA_F16_PEAK_TFS),
+        "a10 MXFP4 qq M=512": mfma_row("qmm_mx512", 2.0 * 512 * 5760 * 2880, FP4_PEAK_TFS),
+        "a10 MXFP4 qq M=32 (weight-streaming size)":
+            hbm_row("qmm_mx32", fp4_bytes(5760, 2880, 32, 32) + 32 * 2880 * 2),
+        "a11 affine weight-only qmm M=2048":
+            mfma_row("qmm_affine", 2.0 * 2048 * INTER * HIDDEN, MFMA_F16_PEAK_TFS),
+        "n1 NVFP4 qq decode M=1": hbm_row("qq_decode", fp4_bytes(INTER, HIDDEN, 16)),
+        "n2 dense prefill path M=2048":
+            mfma_row("dense_2048", 2.0 * 2048 * INTER * HIDDEN, MFMA_F16_PEAK_TFS),
+        "n3 MXFP8 qmv [25600,5120] M=1": hbm_row("qmv_mxfp8", var_bytes("mxfp8")),
+        "n4 NVFP4 stochastic-rounding quantize [4096,5120]":
+            hbm_row("act_quant_sr", NX * (2 * 2 + 4) + NX // 2 + NX // 16),
+    }
+    out["row_rooflines"] = {k: v for k, v in rows.items() if v is not None}
+
     if not args.no_cpu_baseline and out["value"] is not None:
         out["cpu_baseline"] = cpu_baseline(log)
     print(json.dumps(out), flush=True)
