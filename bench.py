@@ -8,8 +8,9 @@ already resident in HBM:
               E4M3 scales + global scale), 1 % outliers at +-20: a burst of
               9 calls over 8 distinct copies of X (cold), per call
   act_quant_warm  the same, 8 calls on one X (warm), per call
-  dequant     NVFP4 dequantize of the same tensor
+  dequant     NVFP4 dequantize of the same tensor (burst of 8 calls, per call)
   w_quant     MXFP4 quantize W[5760,2880] and affine quantize W[1024,512]
+              (burst of 8 pairs over 8 distinct copies of W, per pair)
   act_quant_sr  NVFP4 quantize of the same X with stochastic rounding (one
               random word per element, drawn on the device beforehand)
   qmv_sweep   affine g64 decode GEMV over 64 layers x {gate, up, down}
@@ -27,6 +28,7 @@ already resident in HBM:
               dequantized exactly, then the GEMV; alpha = g_x g_w): a burst of
               8 calls over 4 distinct weight matrices, reported per call
   qmm_mx32 / qmm_mx512   MXFP4 qq GEMM on the scaled MFMA, W[5760,2880]
+              (bursts of 8 calls, per call; M = 32 over distinct copies of W)
   qmm_affine  affine weight-only x[2048,5120] . W_up[25600,5120]^T
   qmv_<fmt>    decode GEMV (M = 1) on W[25600,5120] in each format variant:
               mxfp8, affine 4-bit groups 32 / 128, affine 8-bit groups
@@ -186,12 +188,20 @@ def main():
     def st_act_quant_sr():
         b.quantize(X_act, b.NVFP4, "compute", out=q_act_sr, rbits=rbits_act)
 
+    # dequantize and weight quantize run as bursts of SHORTN calls, per call;
+    # the MXFP4 weight quantize over SHORTN distinct copies of W (265 MB)
+    SHORTN = 8
+    W_mx_copies = [W_mx_bf] + [torch.roll(W_mx_bf, shifts=32 * i, dims=1).contiguous()
+                               for i in range(1, SHORTN)]
+
     def st_dequant():
-        b.dequantize(q_act, out=dq_act)
+        for _ in range(SHORTN):
+            b.dequantize(q_act, out=dq_act)
 
     def st_w_quant():
-        b.quantize(W_mx_bf, b.MXFP4, out=q_mx_out)
-        b.quantize(W_small, b.AFFINE, out=q_small_out)
+        for Wi in W_mx_copies[1:] + W_mx_copies[:1]:  # q_mx_out ends with W's own codes
+            b.quantize(Wi, b.MXFP4, out=q_mx_out)
+            b.quantize(W_small, b.AFFINE, out=q_small_out)
 
     # The sweep's GEMV launches run back to back on one stream, between one
     # pair of HIP events: the mean launch duration is the sweep's time over
@@ -228,7 +238,8 @@ def main():
     # of these stages are per call.
     BURST, NDIST = 8, 4
     per_call = {"qq_decode": BURST,  # stage -> calls per timed burst
-                "act_quant": ACTN + 1, "act_quant_warm": ACTN}
+                "act_quant": ACTN + 1, "act_quant_warm": ACTN, "dequant": SHORTN,
+                "w_quant": SHORTN, "qmm_mx32": SHORTN, "qmm_mx512": SHORTN}
     q_dec = [q_pf] + [b.quantize(S.torch_normal_bf16((INTER, HIDDEN), 0.02, 910 + i, dev),
                                  b.NVFP4) for i in range(NDIST - 1)]
 
@@ -236,8 +247,14 @@ def main():
         for i in range(BURST):
             b.qmm(x_nv1, q_dec[i % NDIST], act="same", workspace=ws_dec, out=y_nv1)
 
+    # MXFP4 qq GEMM as a burst of SHORTN calls, per call: at M = 32 (a
+    # weight-streaming size) over distinct weight copies, at M = 512 on one W
     def mx(M):
-        return lambda: b.qmm(x_mx[M], q_mx, act="same", workspace=ws_mx[M], out=y_mx[M])
+        def run():
+            for i in range(SHORTN):
+                q = q_mx_rot[i] if M <= 32 else q_mx
+                b.qmm(x_mx[M], q, act="same", workspace=ws_mx[M], out=y_mx[M])
+        return run
 
     # decode GEMV on 4-bit float weights: MXFP4 W[5760,2880] at M = 1 and 8
     # over MXROT distinct copies, NVFP4 W[25600,5120] at M = 1 over the qq
@@ -442,8 +459,6 @@ def main():
 
     # Every hot-path row against the roofline that bounds it: algorithmic bytes
     # (HBM rows) or 2*M*N*K flops (MFMA rows) over the stage's time per call.
-    # Short stages timed as one call on an idle queue (dequant, w_quant,
-    # qmm_mx32, qmm_mx512) include the host side of the call.
     def hbm_row(stage, nbytes):
         if stage in ms:
             a = nbytes / (ms[stage] * 1e-3) / 1e9
