@@ -49,6 +49,26 @@ def check_qq(o, b, x, qo, tol=QQ_TOL):
 SHAPES = [(1, 70, 64), (37, 300, 320), (130, 257, 1024), (300, 513, 5120 // 4)]
 
 
+@pytest.mark.parametrize("M,K", [(9, 64), (130, 1024), (2048, 5120)])
+def test_qq_nvfp4_workspace_amax_and_g(oracle_mod, bsfp, M, K):
+    """The NVFP4 qq GEMM path leaves amax(x) and g_x = amax/2688 in the first
+    two floats of its workspace (taken from per-workgroup partial maxima of
+    |x|); both bit-exact against the oracle, also over a workspace that held
+    garbage before the call."""
+    x = S.generic((M, K), 1.0, seed=500 + M)
+    x[M // 2, K // 3] = 0xC1A0  # bf16 -20: one outlier sets the maximum
+    w = S.generic((96, K), 0.02, seed=501)
+    qd = oracle_to_dev(bsfp, oracle_mod, oracle_mod.quantize(2, w))
+    ws = torch.full((bsfp.qmm_workspace_bytes(2, M, K, "same"),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    bsfp.qmm(to_dev(x), qd, act="same", workspace=ws)
+    torch.cuda.synchronize()
+    head = ws[:8].cpu().numpy().view(np.float32)
+    a = oracle_mod.amax(x)
+    assert head[0] == a == np.float32(20.0)
+    assert head[1] == oracle_mod.global_scale(a)
+
+
 @pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_weight_only_ragged(oracle_mod, bsfp, mode, M, N, K):
