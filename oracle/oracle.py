@@ -20,7 +20,9 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# BSFP_ORACLE_LIB names another build of the same source (the mutation check
+# in tests/ loads copies with one planted mistake each); default: this build.
+LIB_PATH = os.environ.get("BSFP_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 AFFINE, MXFP4, NVFP4, MXFP8 = 0, 1, 2, 3
 GROUP = {AFFINE: 64, MXFP4: 32, NVFP4: 16, MXFP8: 32}

@@ -267,3 +267,10 @@ def test_amax_matches_numpy(oracle_mod):
     assert oracle_mod.amax(x) == np.float32(np.abs(oracle_mod.bf16_to_f32(x)).max())
     q = oracle_mod.quantize(oracle_mod.NVFP4, x)
     assert q.amax == oracle_mod.amax(x)
+    # the maximum at the first, a middle and the last position, either sign
+    # (bf16 0x4200 = 32, 0xC200 = -32, above every N(0, 3^2) draw here)
+    for pos in (0, x.size // 2, x.size - 1):
+        for bits in (0x4200, 0xC200):
+            y = x.copy().reshape(-1)
+            y[pos] = bits
+            assert oracle_mod.amax(y.reshape(x.shape)) == np.float32(32.0), (pos, bits)

@@ -132,3 +132,50 @@ def test_mxfp8_saturates(oracle_mod):
     q = o.quantize(3, to_bf16_bits(row).reshape(1, 32))
     c = unpack(q)[0]
     assert q.scales[0, 0] == 127 and c[3] == 0x7E and c[9] == 0xFE
+
+
+def _bf16_bits_of(v):
+    """fp32 values -> bf16 bit patterns by torch's nearest-even conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_affine_variant_dequantize_pinned(oracle_mod, bits, group):
+    """bo_dequantize_g's affine branch against the rule R8 written out here
+    with no oracle codec: codes unpacked by this test (element k at bit
+    bits*(k % (32/bits)) of word k/(32/bits)), scale and bias decoded by
+    torch, s*q + b formed in fp64 (s*q has at most 16 significant bits and
+    the magnitudes below keep the sum exact), rounded once to fp32 (the
+    single rounding of fma) and then to bf16 by torch.  Random codes over
+    the whole range and random scales and biases of both signs, with groups
+    whose fp32 rounding matters (|b| much larger than s*q), so a wrong group
+    index, nibble order, a bias with the wrong sign or an early bf16
+    rounding of s*q fails here."""
+    o = oracle_mod
+    rng = np.random.default_rng(1000 + 10 * bits + group)
+    rows, cols = 7, 4 * group
+    per = 32 // bits
+    codes = rng.integers(0, 2 ** 32, (rows, cols // per), dtype=np.uint64).astype(np.uint32)
+    ng = cols // group
+    s = (rng.uniform(0.25, 1.0, (rows, ng)) * 2.0 ** rng.integers(-14, 2, (rows, ng)))
+    b = rng.uniform(-1.0, 1.0, (rows, ng)) * 2.0 ** rng.integers(-6, 9, (rows, ng))
+    s[0, 0] = 0.0   # a constant group: every value is the bias
+    b[1, 1] = 0.0
+    s[2, 0], b[2, 0] = 0.75 * 2.0 ** -20, 201.0  # s*q + b needs more than 24 bits
+    s_bits = _bf16_bits_of(s.astype(np.float32))
+    b_bits = _bf16_bits_of(b.astype(np.float32))
+    q = o.QTensor(0, rows, cols, codes, s_bits, b_bits, bits=bits, group=group)
+    got = o.dequantize(q)
+    c = unpack(q).astype(np.float64)
+    sv = np.repeat(bf16_f64(s_bits), group, axis=1)
+    bv = np.repeat(bf16_f64(b_bits), group, axis=1)
+    exact = sv * c + bv
+    want = _bf16_bits_of(exact.astype(np.float32))
+    assert np.array_equal(got, want)
+    # the fp32 step matters for some elements (else the pin would not see
+    # a skipped fp32 rounding)
+    assert np.any(exact.astype(np.float32).astype(np.float64) != exact)
+    # and the exact dequantized values are the same s*q + b
+    assert np.array_equal(o.dequant_exact(q), exact)
