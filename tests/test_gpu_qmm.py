@@ -169,17 +169,27 @@ def test_qq_decode_and_gemm_paths_agree(oracle_mod, bsfp, mode):
     assert np.max(np.abs(a - c) / den) <= 2 * QQ_TOL
 
 
-def _sampled_qq(o, b, M, N, K, seed, n_rows=8, n_pairs=2048, x=None, w=None):
+# Full-size prefill checks sample 64 whole output rows plus 4096 random
+# (m, n) outputs; the oracle computes each one on its own.
+N_ROWS, N_PAIRS = 64, 4096
+
+
+def _sample_pairs(M, N, seed, n_rows=N_ROWS, n_pairs=N_PAIRS):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(M, n_rows, replace=False)
+    ai = np.concatenate([np.repeat(rows, N), rng.integers(0, M, n_pairs)])
+    bi = np.concatenate([np.tile(np.arange(N), n_rows), rng.integers(0, N, n_pairs)])
+    return ai, bi
+
+
+def _sampled_qq(o, b, M, N, K, seed, x=None, w=None):
     if x is None:
         x, w = S.nvfp4_prefill(M=M, N=N, K=K, seed=seed)
     qo = o.quantize(2, w)
     y = qmm_dev(o, b, x, qo, "same")
     qx = o.quantize(2, x)  # alpha needs the full-tensor g_x
     alpha = o.alpha(qx.g, qo.g)
-    rng = np.random.default_rng(seed)
-    rows = rng.choice(M, n_rows, replace=False)
-    a_rows = np.concatenate([np.repeat(rows, N), rng.integers(0, M, n_pairs)])
-    bi = np.concatenate([np.tile(np.arange(N), n_rows), rng.integers(0, N, n_pairs)])
+    a_rows, bi = _sample_pairs(M, N, seed)
     uniq_a, inv_a = np.unique(a_rows, return_inverse=True)
     uniq_b, inv_b = np.unique(bi, return_inverse=True)
     A = o.dequant_exact(qx, with_g=False, rows=uniq_a)
@@ -190,33 +200,70 @@ def _sampled_qq(o, b, M, N, K, seed, n_rows=8, n_pairs=2048, x=None, w=None):
     return e
 
 
+def _sampled_wonly(o, b, x, qo, seed):
+    M, N = x.shape[0], qo.rows
+    y = qmm_dev(o, b, x, qo, "bf16")
+    ai, bi = _sample_pairs(M, N, seed)
+    ua, ia = np.unique(ai, return_inverse=True)
+    ub, ib = np.unique(bi, return_inverse=True)
+    A = o.bf16_to_f64(x[ua])
+    B = o.dequant_exact(qo, rows=ub)
+    yref, den = o.matmul_pairs(A, B, ia, ib)
+    return o.norm_err(y[ai, bi], yref, den)
+
+
 @pytest.mark.parametrize("M", [1134, 2048, 4096])
 def test_nvfp4_prefill_qq_sampled_full_size(oracle_mod, bsfp, M):
-    """X[M,5120] x W[25600,5120]^T at full size: 8 full output rows plus
-    2048 random outputs computed one by one by the oracle.  At M = 2048 and
+    """X[M,5120] x W[25600,5120]^T at full size: 64 full output rows plus
+    4096 random outputs computed one by one by the oracle.  At M = 2048 and
     4096 the last 1024 output columns come from the second (small-tile)
     launch; the full rows cover them."""
     e = _sampled_qq(oracle_mod, bsfp, M, 25600, 5120, seed=5)
     assert e.max() <= QQ_TOL, e.max()
 
 
+@pytest.mark.parametrize("M", [1134, 2048, 4096])
+def test_nvfp4_prefill_weight_only_sampled_full_size(oracle_mod, bsfp, M):
+    """NVFP4 weight-only x[M,5120] . W[25600,5120]^T (bf16 x, W's global
+    scale applied to the fp32 sums) at full size, sampled as above.  At
+    M = 2048 and 4096 on 256 CUs the 256 x 256 tiles cover the first 24576
+    output columns and the second launch (128 x 64 tiles) the last 1024;
+    the 64 full rows span both."""
+    o = oracle_mod
+    x, w = S.nvfp4_prefill(M=M, N=25600, K=5120, seed=5)
+    e = _sampled_wonly(o, bsfp, x, o.quantize(2, w), seed=55)
+    assert e.max() <= TOL, e.max()
+
+
+# 2048 rows x 8448 columns make 8 x 33 = 264 tiles of 256 x 256: on 256 CUs
+# one whole round plus 8 tiles, so the first 8192 columns run on the big
+# tiles and the last 256 on the second launch's 128 x 64 tiles.  K = 128
+# keeps the full oracle product small.
+TAIL_SPLIT = (2048, 8448, 128)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_weight_only_tail_split_full(oracle_mod, bsfp, mode):
+    M, N, K = TAIL_SPLIT
+    x = S.generic((M, K), 1.0, seed=1700 + mode)
+    w = S.generic((N, K), 0.02, seed=1710 + mode)
+    check_wonly(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+def test_qq_nvfp4_tail_split_full(oracle_mod, bsfp):
+    M, N, K = TAIL_SPLIT
+    x = S.generic((M, K), 0.02, seed=1720)
+    w = S.generic((N, K), 0.02, seed=1721)
+    check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(2, w))
+
+
 def test_affine_weight_only_extra_shape_sampled(oracle_mod, bsfp):
     """x[2048,5120] . W_up[25600,5120]^T, affine weight-only, sampled (the
-    sample spans both the big-tile and the small-tile column ranges)."""
+    64 full rows span both the big-tile and the small-tile column ranges)."""
     o = oracle_mod
     x = S.generic((2048, 5120), 1.0, seed=6)
     _, w = S.affine_decode("up")
-    qo = o.quantize(0, w)
-    y = qmm_dev(o, bsfp, x, qo, "bf16")
-    rng = np.random.default_rng(6)
-    ai = rng.integers(0, 2048, 4096)
-    bi = rng.integers(0, 25600, 4096)
-    ua, ia = np.unique(ai, return_inverse=True)
-    ub, ib = np.unique(bi, return_inverse=True)
-    A = o.bf16_to_f64(x[ua])
-    B = o.dequant_exact(qo, rows=ub)
-    yref, den = o.matmul_pairs(A, B, ia, ib)
-    e = o.norm_err(y[ai, bi], yref, den)
+    e = _sampled_wonly(o, bsfp, x, o.quantize(0, w), seed=6)
     assert e.max() <= TOL, e.max()
 
 
@@ -345,18 +392,15 @@ def test_dense_deterministic(bsfp):
 
 @pytest.mark.parametrize("M", [1134, 2048])
 def test_dense_prefill_sampled_full_size(oracle_mod, bsfp, M):
-    """X[M,5120] . W[25600,5120]^T (NVFP4, global scale) at full size: 8 full
-    output rows plus 2048 random outputs against the oracle's dense
+    """X[M,5120] . W[25600,5120]^T (NVFP4, global scale) at full size: 64 full
+    output rows plus 4096 random outputs against the oracle's dense
     reference, computed one by one."""
     o = oracle_mod
     x, w = S.nvfp4_prefill(M=M, N=25600, K=5120, seed=7)
     qo = o.quantize(2, w)
     qd = oracle_to_dev(bsfp, o, qo)
     y = from_dev(bsfp.qmm_dense(to_dev(x), qd))
-    rng = np.random.default_rng(7)
-    rows = rng.choice(M, 8, replace=False)
-    ai = np.concatenate([np.repeat(rows, 25600), rng.integers(0, M, 2048)])
-    bi = np.concatenate([np.tile(np.arange(25600), 8), rng.integers(0, 25600, 2048)])
+    ai, bi = _sample_pairs(M, 25600, seed=7)
     ua, ia = np.unique(ai, return_inverse=True)
     ub, ib = np.unique(bi, return_inverse=True)
     A = o.bf16_to_f64(x[ua])
