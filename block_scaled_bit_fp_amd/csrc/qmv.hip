@@ -618,12 +618,15 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
           const float xsum = AFF ? xs[(m * NJ + jc) * 32 + lt] : 0.0f;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const uint4 w = ring[u][r].w;
+            // a lane past the row's last chunk (RAGGED) loaded the next row's
+            // codes: zero them, so that a NaN code there (an E4M3 byte
+            // 0x7F / 0xFF) cannot reach this row's sum through 0 * NaN
+            const uint4 w = valid ? ring[u][r].w : make_uint4(0u, 0u, 0u, 0u);
             if constexpr (AFF && BITS == 8) {
               // 8-bit affine: q = lo + 16 hi over the two nibble planes of
               // each byte, each converted exactly (E4M3 byte trick); x in
               // natural order, element k of a word in byte k % 4
-              const uint4 w2 = ring[u][r].w2;
+              const uint4 w2 = valid ? ring[u][r].w2 : make_uint4(0u, 0u, 0u, 0u);
               const uint32_t ww[8] = {w.x, w.y, w.z, w.w, w2.x, w2.y, w2.z, w2.w};
               const uint32_t xx[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                                        x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
@@ -641,7 +644,7 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
               acc[r][m] = __builtin_fmaf(__uint_as_float(bv[r] << 16), xsum, acc[r][m]);
             } else if constexpr (MODE == FMT_MXFP8) {
               // E4M3 bytes -> bf16 pairs (exact), one E8M0 scale per chunk
-              const uint4 w2 = ring[u][r].w2;
+              const uint4 w2 = valid ? ring[u][r].w2 : make_uint4(0u, 0u, 0u, 0u);
               const uint32_t ww[8] = {w.x, w.y, w.z, w.w, w2.x, w2.y, w2.z, w2.w};
               const uint32_t xx[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                                        x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};

@@ -116,3 +116,26 @@ def test_variant_fused_qmm_points_to_dense(bsfp):
     with pytest.raises(bsfp.BsfpError) as ei:
         bsfp.qmm(x, q)
     assert ei.value.status == 2 and "bsfp_qmm_dense" in str(ei.value)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_variant_qmv_ragged_nan_codes_stay_in_their_row(oracle_mod, bsfp, M):
+    """MXFP8 at K = 2880 (90 chunks of 32, not whole 32-chunk steps): the
+    lanes past a row's last chunk load the next row's first codes.  With
+    E4M3 NaN bytes (0x7F) planted in the first 6 chunks of every odd row,
+    every even row must still match the oracle (a format's NaN code is data
+    the contract accepts; it may only reach its own row)."""
+    o = oracle_mod
+    K, N = 2880, 64
+    x = S.generic((M, K), 1.0, seed=440 + M)
+    w = S.generic((N, K), 0.02, seed=441)
+    qo = o.quantize(3, w)
+    codes = qo.codes.copy()
+    codes[1::2, :48] = 0x7F7F7F7F  # 192 code bytes = 6 chunks of 32 elements
+    qo.codes = codes
+    y = from_dev(bsfp.qmv(to_dev(x), oracle_to_dev(bsfp, o, qo)))
+    yref, den = o.matmul_wonly(x, qo)
+    ye, re, de = y[:, 0::2], yref[:, 0::2], den[:, 0::2]
+    assert np.all(np.isfinite(re))
+    e = o.norm_err(ye, re, de)
+    assert e.max() <= TOL, (e.max(), np.unravel_index(e.argmax(), e.shape))
