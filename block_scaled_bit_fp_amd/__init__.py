@@ -179,6 +179,32 @@ def _as_2d_bf16(x: torch.Tensor) -> torch.Tensor:
     return x.reshape(-1, x.shape[-1]) if x.dim() != 2 else x
 
 
+def _out_bf16(out: Optional[torch.Tensor], shape, device) -> torch.Tensor:
+    """A caller's output buffer: checked before any pointer crosses the C ABI
+    (which cannot know buffer sizes), or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be bf16 of shape {tuple(shape)}, got {out.dtype} "
+                         f"{tuple(out.shape)}")
+    if not out.is_cuda or out.device != torch.device(device) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous tensor on {device}")
+    return out
+
+
+def _buffer(t: Optional[torch.Tensor], need: int, device, what: str) -> Optional[torch.Tensor]:
+    """A caller's workspace or scratch of at least `need` bytes, or a new one."""
+    if t is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    if not t.is_cuda or t.device != torch.device(device) or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous tensor on {device}")
+    return t
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """max |x| as a device fp32 [1] tensor."""
     if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
@@ -208,6 +234,13 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
             if g is None:
                 raise ValueError("global_scale='given' needs g")
             out.global_scale.copy_(g.reshape(1).to(torch.float32))
+    else:
+        if out.mode != mode or (out.rows, out.cols) != (rows, cols):
+            raise ValueError(f"out holds mode {out.mode} [{out.rows}, {out.cols}], the call "
+                             f"asks for mode {mode} [{rows}, {cols}]")
+        if (bits is not None and bits != out.nbits) or (group is not None and
+                                                         group != out.group_size):
+            raise ValueError("out's bits or group size differ from the ones asked for")
     if mode == NVFP4 and gs == GS_NONE:
         out.global_scale = None
     d = out.desc()
@@ -222,8 +255,7 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
 
 
 def dequantize(q: QuantizedTensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    if out is None:
-        out = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.codes.device)
+    out = _out_bf16(out, (q.rows, q.cols), q.codes.device)
     d = q.desc()
     _check(lib().bsfp_dequantize(C.byref(d), _ptr(out), _stream()))
     return out
@@ -235,8 +267,7 @@ def qmv(x: torch.Tensor, w: QuantizedTensor, out: Optional[torch.Tensor] = None)
     M = x2.shape[0]
     if x2.shape[1] != w.cols:
         raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
-    if out is None:
-        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    out = _out_bf16(out, (M, w.rows), x.device)
     d = w.desc()
     _check(lib().bsfp_qmv(_ptr(x2), M, C.byref(d), _ptr(out), _stream()))
     return out
@@ -259,13 +290,11 @@ def qmm_dense(x: torch.Tensor, w: QuantizedTensor, scratch: Optional[torch.Tenso
     if x2.shape[1] != w.cols:
         raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
     need = qmm_dense_scratch_bytes(w.rows, w.cols)
-    if scratch is None:
-        scratch = torch.empty(need, dtype=torch.uint8, device=x.device)
-    if out is None:
-        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    scratch = _buffer(scratch, need, x.device, "scratch")
+    out = _out_bf16(out, (M, w.rows), x.device)
     d = w.desc()
-    _check(lib().bsfp_qmm_dense(_ptr(x2), M, C.byref(d), _ptr(scratch),
-                                scratch.numel() * scratch.element_size(), _ptr(out), _stream()))
+    _check(lib().bsfp_qmm_dense(_ptr(x2), M, C.byref(d), _ptr(scratch), _nbytes(scratch),
+                                _ptr(out), _stream()))
     return out
 
 
@@ -284,11 +313,10 @@ def qmm(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
         return qmm_dense(x2, w, scratch=scratch, out=out)
     a = ACT_SAME if act == "same" else ACT_BF16
     need = int(lib().bsfp_qmm_workspace_bytes(w.mode, M, w.cols, a))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    if out is None:
-        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    workspace = _buffer(workspace, need, x.device, "workspace")
+    out = _out_bf16(out, (M, w.rows), x.device)
     d = w.desc()
-    _check(lib().bsfp_qmm(_ptr(x2), M, C.byref(d), a, _ptr(workspace),
-                          0 if workspace is None else workspace.numel(), _ptr(out), _stream()))
+    _check(lib().bsfp_qmm(_ptr(x2), M, C.byref(d), a, _ptr(workspace), _nbytes(workspace),
+                          _ptr(out), _stream()))
     return out
+
