@@ -32,7 +32,10 @@ STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_E
 EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
            "bsfp_quantize_sr", "bsfp_qmm_workspace_bytes", "bsfp_qmm",
            "bsfp_qmm_dense_scratch_bytes",
-           "bsfp_qmm_dense", "bsfp_time_next_launch", "bsfp_last_error", "bsfp_version")
+           "bsfp_qmm_dense", "bsfp_qmm_noalloc", "bsfp_time_next_launch", "bsfp_last_error",
+           "bsfp_version")
+# bytes of bsfp_qmm_noalloc's static device workspace (BSFP_NOALLOC_WORKSPACE_BYTES)
+NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 
 class QTensorDesc(C.Structure):
@@ -72,6 +75,7 @@ def lib():
             "bsfp_qmm": (C.c_int, [P, I64, QP, I32, P, C.c_size_t, P, P]),
             "bsfp_qmm_dense_scratch_bytes": (C.c_size_t, [I64, I64]),
             "bsfp_qmm_dense": (C.c_int, [P, I64, QP, P, C.c_size_t, P, P]),
+            "bsfp_qmm_noalloc": (C.c_int, [P, I64, QP, I32, P, P]),
             "bsfp_time_next_launch": (C.c_int, [P, P]),
             "bsfp_last_error": (C.c_char_p, []),
             "bsfp_version": (C.c_char_p, []),
@@ -320,3 +324,19 @@ def qmm(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
                           _ptr(out), _stream()))
     return out
 
+
+def qmm_noalloc(x: torch.Tensor, w: QuantizedTensor, act: str = "bf16",
+                out: torch.Tensor = None) -> torch.Tensor:
+    """qmm whose qq workspace is the library's static device array
+    (bsfp_qmm_noalloc): the C call allocates nothing.  Pass `out` to keep
+    the whole call free of allocations.  Calls that overlap on one GPU share
+    that array and must be serialized by the caller."""
+    x2 = _as_2d_bf16(x)
+    M = x2.shape[0]
+    if x2.shape[1] != w.cols:
+        raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    out = _out_bf16(out, (M, w.rows), x.device)
+    a = ACT_SAME if act == "same" else ACT_BF16
+    d = w.desc()
+    _check(lib().bsfp_qmm_noalloc(_ptr(x2), M, C.byref(d), a, _ptr(out), _stream()))
+    return out

@@ -130,6 +130,50 @@ int device_max_lds() {
 
 }  // namespace bsfp
 
+// ---------------------------------------------------------------------------
+// bsfp_qmm_noalloc: bsfp_qmm with the workspace in the library's own device
+// memory, for callers that cannot allocate.  `scratch` is a file-scope device
+// array (one copy per GPU, held until the process ends).  In host code its
+// name is only a stand-in: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch_ptr, and
+// only that pointer is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[BSFP_NOALLOC_WORKSPACE_BYTES];
+
+namespace bsfp {
+namespace {
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {nullptr};
+
+// The device address of `scratch` on the current device (nullptr and a
+// message on failure).
+void* scratch_ptr(const char* fn, bsfp_status* st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = fail(BSFP_ERR_DEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    *st = fail(BSFP_ERR_UNSUPPORTED, "%s: device %d beyond the 64 the library tracks", fn, dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *st = fail(BSFP_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                 hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *st = BSFP_OK;
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace bsfp
+
 using namespace bsfp;
 
 extern "C" {
@@ -242,45 +286,79 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
   return qmm_workspace_bytes(mode, M, K, act);
 }
 
-bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_t act,
-                     void* workspace, size_t workspace_bytes, uint16_t* y, bsfp_stream stream) {
-  bsfp_status st = check_qtensor(w, "bsfp_qmm");
+// Argument checks of bsfp_qmm and bsfp_qmm_noalloc (everything but the
+// workspace).  *done is set when the call has nothing to compute.
+static bsfp_status check_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_t act,
+                             const uint16_t* y, const char* fn, bool* done) {
+  *done = false;
+  bsfp_status st = check_qtensor(w, fn);
   if (st != BSFP_OK) return st;
   if (is_variant(w))
     return fail(BSFP_ERR_UNSUPPORTED,
-                "bsfp_qmm: %s %d-bit group %d runs on the dense path (bsfp_qmm_dense)",
+                "%s: %s %d-bit group %d runs on the dense path (bsfp_qmm_dense)", fn,
                 mode_name(w->mode), (int)w->bits, (int)w->group_size);
-  if (M < 0) return fail(BSFP_ERR_ARG, "bsfp_qmm: negative M");
+  if (M < 0) return fail(BSFP_ERR_ARG, "%s: negative M", fn);
   if (act != BSFP_ACT_BF16 && act != BSFP_ACT_SAME)
-    return fail(BSFP_ERR_ARG, "bsfp_qmm: bad activation mode %d", (int)act);
-  if (M == 0 || w->rows == 0) return ok();
-  if (w->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmm: K must be positive");
-  if (!x || !aligned16(x)) return fail(BSFP_ERR_ARG, "bsfp_qmm: x is null or not 16-byte aligned");
-  if (!y || !aligned16(y)) return fail(BSFP_ERR_ARG, "bsfp_qmm: y is null or not 16-byte aligned");
+    return fail(BSFP_ERR_ARG, "%s: bad activation mode %d", fn, (int)act);
+  if (M == 0 || w->rows == 0) {
+    *done = true;
+    return ok();
+  }
+  if (w->cols == 0) return fail(BSFP_ERR_ARG, "%s: K must be positive", fn);
+  if (!x || !aligned16(x)) return fail(BSFP_ERR_ARG, "%s: x is null or not 16-byte aligned", fn);
+  if (!y || !aligned16(y)) return fail(BSFP_ERR_ARG, "%s: y is null or not 16-byte aligned", fn);
   if (w->cols % 64)
-    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld is not a multiple of 64",
+    return fail(BSFP_ERR_UNSUPPORTED, "%s: K = %lld is not a multiple of 64", fn,
                 (long long)w->cols);
   if ((reinterpret_cast<uintptr_t>(w->scales) & 3) ||
       (w->biases && (reinterpret_cast<uintptr_t>(w->biases) & 3)))
-    return fail(BSFP_ERR_ARG, "bsfp_qmm: scales and biases must be 4-byte aligned");
+    return fail(BSFP_ERR_ARG, "%s: scales and biases must be 4-byte aligned", fn);
   if (act == BSFP_ACT_SAME && w->mode == BSFP_AFFINE)
     return fail(BSFP_ERR_UNSUPPORTED,
-                "bsfp_qmm: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only");
+                "%s: BSFP_ACT_SAME is supported for nvfp4 and mxfp4 weights only", fn);
   if (M > (1 << 30) || w->rows > (1 << 30))
-    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: M or N beyond 2^30");
+    return fail(BSFP_ERR_UNSUPPORTED, "%s: M or N beyond 2^30", fn);
   // every launch shape keeps its grid under 2^32 threads up to 2^33 outputs
   if ((uint64_t)M * (uint64_t)w->rows > (1ULL << 33))
-    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: M * N = %llu beyond 2^33",
+    return fail(BSFP_ERR_UNSUPPORTED, "%s: M * N = %llu beyond 2^33", fn,
                 (unsigned long long)M * (unsigned long long)w->rows);
   // the GEMM addresses a 256-row activation tile with 32-bit byte offsets
   if (w->cols > (1 << 22))
-    return fail(BSFP_ERR_UNSUPPORTED, "bsfp_qmm: K = %lld beyond 2^22",
-                (long long)w->cols);
+    return fail(BSFP_ERR_UNSUPPORTED, "%s: K = %lld beyond 2^22", fn, (long long)w->cols);
+  return ok();
+}
+
+bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_t act,
+                     void* workspace, size_t workspace_bytes, uint16_t* y, bsfp_stream stream) {
+  bool done = false;
+  const bsfp_status st = check_qmm(x, M, w, act, y, "bsfp_qmm", &done);
+  if (st != BSFP_OK || done) return st;
   const size_t need = qmm_workspace_bytes(w->mode, M, w->cols, act);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(BSFP_ERR_ARG, "bsfp_qmm: workspace needs %zu bytes (16-byte aligned), got %zu",
                 need, workspace_bytes);
   return device_status(launch_qmm(x, M, *w, act, workspace, y, (hipStream_t)stream), "bsfp_qmm");
+}
+
+bsfp_status bsfp_qmm_noalloc(const uint16_t* x, int64_t M, const bsfp_qtensor* w, int32_t act,
+                             uint16_t* y, bsfp_stream stream) {
+  bool done = false;
+  bsfp_status st = check_qmm(x, M, w, act, y, "bsfp_qmm_noalloc", &done);
+  if (st != BSFP_OK || done) return st;
+  const size_t need = qmm_workspace_bytes(w->mode, M, w->cols, act);
+  if (need > (size_t)BSFP_NOALLOC_WORKSPACE_BYTES)
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_qmm_noalloc: this product needs a %zu-byte workspace, beyond the %zu "
+                "bytes of the library's static one (M = %lld, K = %lld); use bsfp_qmm with a "
+                "caller workspace", need, (size_t)BSFP_NOALLOC_WORKSPACE_BYTES, (long long)M,
+                (long long)w->cols);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr("bsfp_qmm_noalloc", &st);
+    if (!ws) return st;
+  }
+  return device_status(launch_qmm(x, M, *w, act, ws, y, (hipStream_t)stream),
+                       "bsfp_qmm_noalloc");
 }
 
 size_t bsfp_qmm_dense_scratch_bytes(int64_t rows, int64_t cols) {

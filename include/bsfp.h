@@ -55,7 +55,9 @@
  *   - Tensor pointers are DEVICE pointers of the current HIP device, 16-byte
  *     aligned; bf16 travels as uint16 bit patterns.  The caller owns and
  *     allocates every buffer (the library allocates no device memory, never
- *     frees, and never writes its inputs).
+ *     frees, and never writes its inputs; the one exception is the static
+ *     workspace of bsfp_qmm_noalloc, which lives in the library's code
+ *     object on each GPU).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     with no host synchronization.
  *   - Functions never throw and never abort.  Argument errors are detected on
@@ -216,6 +218,33 @@ size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act)
 bsfp_status bsfp_qmm(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
                      int32_t act, void* workspace, size_t workspace_bytes,
                      uint16_t* y, bsfp_stream stream);
+
+/*
+ * Size of the workspace that bsfp_qmm_noalloc keeps in the library's own
+ * device memory: 32 MiB per GPU.  It holds the qq workspace of
+ * bsfp_qmm_workspace_bytes(...) up to that size, e.g. NVFP4 activations of
+ * up to 2^24 elements (M = 3276 at K = 5120) or MXFP4 ones of up to about
+ * 6.3 * 10^7.
+ */
+#define BSFP_NOALLOC_WORKSPACE_BYTES (32u << 20)
+
+/*
+ * bsfp_qmm_noalloc: bsfp_qmm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, semantics, limits and errors as bsfp_qmm,
+ * except that the workspace is not passed: the call uses a static device
+ * array of BSFP_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU,
+ * held until the process ends (its address on a device is looked up on the
+ * first call there).  The call allocates and frees nothing; the caller still
+ * owns x, w and y.  A product whose workspace would exceed that size returns
+ * BSFP_ERR_UNSUPPORTED and launches nothing.  Every call on one GPU shares
+ * that GPU's array, and it keeps what the last call left there (every byte
+ * a call reads it first writes, so nothing needs to start at zero): calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialized by the caller.
+ */
+bsfp_status bsfp_qmm_noalloc(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
+                             int32_t act, uint16_t* y, bsfp_stream stream);
 
 /*
  * bsfp_qmm_dense_scratch_bytes: bytes of the bf16 copy of a [rows, cols]

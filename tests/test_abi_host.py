@@ -192,3 +192,29 @@ def test_element_count_limit(blib):
                    L.bsfp_qmm(X, 4, C.byref(d), 0, None, 0, X, None)):
             st, msg = status(blib, rc)
             assert st == "BSFP_ERR_UNSUPPORTED" and "2^40" in msg, msg
+
+
+def test_noalloc_checks_before_touching_the_gpu(blib):
+    """bsfp_qmm_noalloc applies bsfp_qmm's argument checks, and refuses a
+    product whose workspace exceeds its static array, before it looks up the
+    array or launches anything."""
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    d = desc(blib, rows=64, cols=5120)
+    assert status(blib, L.bsfp_qmm_noalloc(X, 4, C.byref(d), 5, X, None))[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_qmm_noalloc(None, 4, C.byref(d), 1, X, None))[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_qmm_noalloc(X, 4, C.byref(d), 1, None, None))[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_qmm_noalloc(X, -1, C.byref(d), 1, X, None))[0] == "BSFP_ERR_ARG"
+    # nothing to compute: OK without any GPU work
+    assert status(blib, L.bsfp_qmm_noalloc(X, 0, C.byref(d), 1, X, None))[0] == "BSFP_OK"
+    # NVFP4 qq at M = 3277, K = 5120: 33.6 MB of workspace > 32 MiB
+    M = blib.NOALLOC_WORKSPACE_BYTES // (2 * 5120) + 1
+    assert L.bsfp_qmm_workspace_bytes(2, M, 5120, 1) > blib.NOALLOC_WORKSPACE_BYTES
+    st, msg = status(blib, L.bsfp_qmm_noalloc(X, M, C.byref(d), 1, X, None))
+    assert st == "BSFP_ERR_UNSUPPORTED" and "static" in msg and str(M) in msg, msg
+
+
+def test_noalloc_size_matches_header(blib):
+    text = open(HEADER).read()
+    m = re.search(r"#define BSFP_NOALLOC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == blib.NOALLOC_WORKSPACE_BYTES
