@@ -372,6 +372,7 @@ def main():
                                   "(14.17 GB), plus NVFP4 prefill qqmm X[2048,5120] . "
                                   "W[25600,5120]^T and the other hot-path stages",
                       "arch": "gfx950", "device": props.name}}
+    out["config"]["gpu"] = device_info(props)
     stage_ms = {n: round(v, 4) for n, v in ms.items()}
     out["stages_ms"] = stage_ms
     if "qmv_sweep" in ms:
@@ -563,28 +564,127 @@ def measured_traffic(name, sources):
     return int(float(fields["hbm_bytes_per_launch"]))
 
 
+def host_info():
+    """nproc, CPU model and the oracle's OpenMP thread count on this host."""
+    import ctypes as C
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    gomp = C.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle links
+    return {"nproc": os.cpu_count(), "cpus_usable": len(os.sched_getaffinity(0)),
+            "cpu_model": model, "omp_threads": int(gomp.omp_get_max_threads()),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def device_info(props):
+    """GPU engine clock, CU count, gfx target and the HIP / ROCm versions."""
+    import ctypes as C
+
+    import torch
+    rt = C.CDLL("libamdhip64.so")
+    clk, rtv, drv = C.c_int(0), C.c_int(0), C.c_int(0)
+    rt.hipDeviceGetAttribute(C.byref(clk), 5, 0)  # hipDeviceAttributeClockRate (kHz)
+    rt.hipRuntimeGetVersion(C.byref(rtv))
+    rt.hipDriverGetVersion(C.byref(drv))
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"device": props.name, "gfx": props.gcnArchName.split(":")[0],
+            "cus": props.multi_processor_count, "peak_engine_clock_mhz": clk.value // 1000,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1), "hip_runtime": rtv.value,
+            "hip_driver": drv.value, "rocm": rocm, "torch": torch.__version__,
+            "torch_hip": torch.version.hip}
+
+
 def cpu_baseline(log):
-    """The oracle (plain C, fp64 matmul) on one affine W_up[25600,5120] qmv."""
+    """The oracle (plain C: fp32 quantizer decisions, fp64 dequantize and
+    matmul, OpenMP over outputs in the matmul only) timed on a bounded sample
+    of every workload, once on one thread and once on all of them.  The
+    headline `value` is the affine decode qmv on all threads (the metric's
+    unit); `configs` holds the rest."""
+    import ctypes as C
+
     import numpy as np
 
     import synth_inputs as S
     from oracle import oracle as o
 
-    x, w = S.affine_decode("up")
-    qo = o.quantize(o.AFFINE, w)
-    nbytes = affine_bytes(25600, 5120)
-    reps, t = 0, 0.0
-    while t < 10.0 and reps < 20:
-        t0 = time.perf_counter()
-        o.matmul_wonly(x, qo)
-        t += time.perf_counter() - t0
-        reps += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    gbs = nbytes * reps / t / 1e9
-    log(f"[bench] cpu oracle: {reps} affine qmv of [25600,5120] in {t:.1f}s -> {gbs:.3f} GB/s")
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x affine g64 qmv W_up[25600,5120] (73.8 MB each), fp64 "
-                      "dequantize + fp64 dot products, OpenMP over outputs"}
+    gomp = C.CDLL("libgomp.so.1")
+    all_threads = int(gomp.omp_get_max_threads())
+
+    def timed(fn, min_s=1.0, max_reps=50):
+        fn()  # first call outside the clock (page-in)
+        reps, t = 0, 0.0
+        while (t < min_s and reps < max_reps) or reps == 0:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            reps += 1
+        return t / reps
+
+    def both(fn, work, unit_div):
+        res = {}
+        for label, n in (("single_thread", 1), ("all_threads", all_threads)):
+            gomp.omp_set_num_threads(n)
+            res[label] = round(work / timed(fn) / unit_div, 4)
+        gomp.omp_set_num_threads(all_threads)
+        return res
+
+    cfg = {}
+    # 1: affine qmv x[1,512] . W[1024,512]^T (whole workload)
+    x1, w1 = S.affine_small()
+    q1 = o.quantize(o.AFFINE, w1)
+    cfg["affine_qmv_1024x512"] = {"unit": "GB/s", "sample": "whole workload", **both(
+        lambda: o.matmul_wonly(x1, q1), affine_bytes(1024, 512), 1e9)}
+    # 2: NVFP4 activation amax + quantize, the first 256 of the 4096 rows
+    xa = np.ascontiguousarray(S.nvfp4_activations()[:256])
+    row_bytes = HIDDEN * 2 * 2 + HIDDEN // 2 + HIDDEN // 16
+    cfg["nvfp4_quantize_4096x5120"] = {
+        "unit": "GB/s", "sample": "rows 0..255 of X (amax over the sample, then quantize); "
+        "the quantizer is sequential", **both(lambda: o.quantize(o.NVFP4, xa), 256 * row_bytes,
+                                               1e9)}
+    # 3: affine decode qmv on W_up, the first 2560 of 25600 rows
+    x3, w3 = S.affine_decode("up")
+    q3 = o.quantize(o.AFFINE, np.ascontiguousarray(w3[:2560]))
+    del w3
+    cfg["affine_qmv_25600x5120"] = {"unit": "GB/s", "sample": "rows 0..2559 of W_up",
+                                    **both(lambda: o.matmul_wonly(x3, q3),
+                                           affine_bytes(2560, HIDDEN), 1e9)}
+    # 4: MXFP4 W[5760,2880]: qmv at M = 1 (all rows) and the qq product at
+    # M = 512 on the first 576 weight rows
+    w4 = S.mxfp4_weights()
+    q4 = o.quantize(o.MXFP4, w4)
+    q4s = o.quantize(o.MXFP4, np.ascontiguousarray(w4[:576]))
+    x41, x4 = S.mxfp4_activations(1), S.mxfp4_activations(512)
+    cfg["mxfp4_qmv_m1_5760x2880"] = {"unit": "GB/s", "sample": "whole workload", **both(
+        lambda: o.matmul_wonly(x41, q4), fp4_bytes(5760, 2880, 32, 1), 1e9)}
+    cfg["mxfp4_qq_m512_5760x2880"] = {
+        "unit": "GFLOP/s", "sample": "x[512,2880] against W rows 0..575 (x quantized in the call)",
+        **both(lambda: o.matmul_qq(x4, q4s), 2.0 * 512 * 576 * 2880, 1e9)}
+    # 5: NVFP4 qq prefill, 64 rows of X[2048,5120] against the first 2560 W rows
+    x5, w5 = S.nvfp4_prefill(M=64, N=2560, K=HIDDEN, seed=5)
+    q5 = o.quantize(o.NVFP4, w5)
+    cfg["nvfp4_qqmm_2048x25600x5120"] = {
+        "unit": "GFLOP/s", "sample": "X[64,5120] against W[2560,5120] (x quantized in the call, "
+        "g_x from the sample)", **both(lambda: o.matmul_qq(x5, q5), 2.0 * 64 * 2560 * HIDDEN,
+                                       1e9)}
+    head = cfg["affine_qmv_25600x5120"]
+    log("[bench] cpu oracle: " + ", ".join(
+        f"{k}={v['single_thread']}/{v['all_threads']} {v['unit']}" for k, v in cfg.items()))
+    return {"value": head["all_threads"], "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "sample": "affine g64 qmv x[1,5120] . W_up[2560 of 25600 rows, 5120]^T: fp64 "
+                      "dequantize and dot products, OpenMP over outputs, on all threads; "
+                      "`configs` has every workload on one thread and on all",
+            "single_thread_value": head["single_thread"], "configs": cfg, "host": host_info()}
 
 
 if __name__ == "__main__":
