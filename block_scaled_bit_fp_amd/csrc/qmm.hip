@@ -141,15 +141,27 @@ __device__ __forceinline__ f32x16_t mfma16(const uint4& a, const Op8& b, const f
   }
 }
 
-// XCD-aware tile order: workgroup b runs on XCD b % 8, so consecutive logical
-// tiles (which share a weight column block across the M tiles) are given to
-// workgroups of one XCD and hit the same L2.
-__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {
-  int b = blockIdx.x;
-  const int T = tiles_m * tiles_n;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
-  tm = b % tiles_m;
-  tn = b / tiles_m;
+// XCD-aware tile order.  Workgroup b runs on XCD b % 8, so XCD x gets the
+// count_x = ceil((T - x) / 8) workgroups b = x, x + 8, ...; they are given
+// one contiguous range of logical tiles, [start_x, start_x + count_x), so
+// tiles that share operands share that XCD's L2.  m_major: consecutive
+// logical tiles share an activation row block (the weight column blocks
+// stream past it); otherwise they share a weight column block across the M
+// tiles.
+// m_major = 1 from 16 row blocks up (the 16-bit GEMM at M = 4096 read 3 %
+// faster that way; at M = 1134 the weight-column order was faster).
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int m_major, int& tm,
+                                        int& tn) {
+  const int b = blockIdx.x, T = tiles_m * tiles_n;
+  const int x = b & 7, q = T >> 3, r = T & 7;
+  const int L = x * q + min(x, r) + (b >> 3);
+  if (m_major) {
+    tm = L / tiles_n;
+    tn = L % tiles_n;
+  } else {
+    tm = L % tiles_m;
+    tn = L / tiles_m;
+  }
 }
 
 // Physical 16-byte chunk of logical chunk c in tile row r.  The XOR with r & 7
@@ -176,7 +188,8 @@ __device__ __forceinline__ void load_bfrag_buf(BFrag& f, const rsrc_t& rc, const
 }
 
 // WGM x WGN waves per workgroup, each owning WMT x WNT MFMA tiles of 32 x 32.
-template <int DEC, int WGM, int WGN, int WMT, int WNT>
+// PP: the ping-pong schedule described at the K loop (8 waves, WGM = 2).
+template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
+  tile_of(tiles_m, tiles_n, tiles_m >= 16, tm, tn);
   const int m_base = tm * BM, n_base = tn * BN;
   const int rows_m = min(BM, M - m_base), rows_n = min(BN, N - n_base);
 
@@ -372,17 +385,98 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     mma(3, a1);
   };
 
-  load_step(0, stage(0));
-  load_step(min(1, nsteps - 1), stage(1));
-  int st = 0;
-  for (; st + 3 <= nsteps; st += 3) {
-    step(st, 0, 2);
-    step(st + 1, 1, 0);
-    step(st + 2, 2, 1);
+  if constexpr (PP) {
+    // Ping-pong.  The two waves that share a SIMD (w and w + 4: waves are
+    // dealt to the 4 SIMDs round-robin) belong to different groups, g = w / 4
+    // (= wm), and group 1 runs one phase behind group 0.  Each K step is four
+    // phases separated by workgroup barriers: M (read the A fragments of two
+    // sub-steps from LDS and expand the matching weight words in registers;
+    // the first M of a step also reads the step's codes and scales and issues
+    // the loads of the step after next) and C (the 16 MFMAs of those two
+    // sub-steps), twice.  Between two barriers one wave of every SIMD issues
+    // MFMAs while the other waits on LDS and runs the expansion, so the MFMA
+    // pipe is not left idle while both waves of a SIMD sit in the same
+    // read-and-expand phase.  Data hazards: step s + 1's loads are waited for
+    // (vmcnt) at the end of every wave's second M of step s, before the
+    // barrier that precedes group 0's first read of step s + 1; the loads of
+    // step s + 2 overwrite the stage of step s - 1, whose last reads (group
+    // 1's second M of step s - 1) end before that barrier.
+    static_assert(NW == 8 && WGM == 2 && !DENSE, "ping-pong needs 8 waves in two rows");
+    auto bar = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pp_step = [&](int st, int si, int pi) {
+      const uint4* cur = stage(si);
+      BFrag b[WNT];
+      uint4 a0[WMT], a1[WMT];
+      Op8 e0[WNT], e1[WNT];
+      auto read_a = [&](int kk, uint4 (&a)[WMT]) {
+#pragma unroll
+        for (int i = 0; i < WMT; ++i) {
+          const int r = wm * 32 * WMT + 32 * i + l32;
+          a[i] = cur[r * 8 + swz(r, 4 * h + kk)];
+        }
+      };
+      auto expand_kk = [&](int kk, Op8 (&e)[WNT]) {
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) e[j] = expand<DEC>(b[j], kk);
+      };
+      auto mma = [&](const uint4 (&a)[WMT], const Op8 (&e)[WNT]) {
+#pragma unroll
+        for (int j = 0; j < WNT; ++j)
+#pragma unroll
+          for (int i = 0; i < WMT; ++i) acc[i][j] = mfma16<DEC>(a[i], e[j], acc[i][j]);
+      };
+      read_b(cur, st, b);  // M: sub-steps 0 and 1
+      read_a(0, a0);
+      read_a(1, a1);
+      load_step(min(st + 2, nsteps - 1), stage(pi));
+      expand_kk(0, e0);
+      expand_kk(1, e1);
+      bar();
+      mma(a0, e0);  // C
+      mma(a1, e1);
+      bar();
+      read_a(2, a0);  // M: sub-steps 2 and 3
+      read_a(3, a1);
+      expand_kk(2, e0);
+      expand_kk(3, e1);
+      wait_vmem_le<kStepLoads>();  // step st + 1 has landed
+      bar();
+      mma(a0, e0);  // C
+      mma(a1, e1);
+      bar();
+    };
+    load_step(0, stage(0));
+    load_step(min(1, nsteps - 1), stage(1));
+    wait_vmem_le<kStepLoads>();
+    bar();
+    if (wm == 1) bar();  // group 1 starts one phase behind
+    int st = 0;
+    for (; st + 3 <= nsteps; st += 3) {
+      pp_step(st, 0, 2);
+      pp_step(st + 1, 1, 0);
+      pp_step(st + 2, 2, 1);
+    }
+    if (st < nsteps) pp_step(st, 0, 2);
+    if (st + 1 < nsteps) pp_step(st + 1, 1, 0);
+    if (wm == 0) bar();  // the same number of barriers in both groups
+    wait_vmem();  // the surplus loads land before the LDS is released
+  } else {
+    load_step(0, stage(0));
+    load_step(min(1, nsteps - 1), stage(1));
+    int st = 0;
+    for (; st + 3 <= nsteps; st += 3) {
+      step(st, 0, 2);
+      step(st + 1, 1, 0);
+      step(st + 2, 2, 1);
+    }
+    if (st < nsteps) step(st, 0, 2);
+    if (st + 1 < nsteps) step(st + 1, 1, 0);
+    wait_vmem();  // the surplus loads land before the LDS is released
   }
-  if (st < nsteps) step(st, 0, 2);
-  if (st + 1 < nsteps) step(st + 1, 1, 0);
-  wait_vmem();  // the surplus loads land before the LDS is released
 
   const float sc = (g1 ? *g1 : 1.0f) * (g2 ? *g2 : 1.0f);
   const bool full = (rows_m == BM) && (rows_n == BN);
@@ -408,7 +502,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     }
 }
 
-template <int DEC, int WGM, int WGN, int WMT, int WNT>
+template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false>
 void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int n,
                const float* g1, const float* g2, uint16_t* y, hipStream_t s, hipEvent_t ev0,
                hipEvent_t ev1) {
@@ -421,7 +515,7 @@ void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int 
   const uint32_t* codes = w.codes + n0 * (K / 8);
   const void* scales = reinterpret_cast<const uint8_t*>(w.scales) + n0 * (K / gsz) * sbytes;
   const uint16_t* biases = w.biases ? w.biases + n0 * (K / 64) : nullptr;
-  auto kern = &gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT>;
+  auto kern = &gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT, PP>;
   const dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
   if (ev0 || ev1)
     hipExtLaunchKernelGGL(kern, grid, block, 0u, s, ev0, ev1, 0u, A, codes, scales, biases, g1,
@@ -459,6 +553,9 @@ hipError_t run_dense(const uint16_t* A, int M, const uint16_t* B, int N, int K, 
 // round; instead the weight rows of the whole rounds run with big tiles and
 // the remaining rows in a second launch of 128 x 64 tiles, which spreads
 // them over all CUs.
+// The 256 x 256 prefill tiles run the ping-pong schedule.
+constexpr bool kPingPong = true;
+
 template <int DEC>
 hipError_t run_dq_big(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
                       const float* g2, uint16_t* y, hipStream_t s) {
@@ -471,10 +568,10 @@ hipError_t run_dq_big(const uint16_t* A, int M, const bsfp_qtensor& w, const flo
   const int n_main = (int)std::min<int64_t>(tiles_n, rounds * cus / tiles_m) * 256;
   const LaunchEvents ev = take_launch_events();
   if (rounds == 0 || rest * 2 > cus || n_main <= 0 || n_main >= N) {
-    launch_dq<DEC, 2, 4, 4, 2>(A, M, w, 0, N, g1, g2, y, s, ev.start, ev.stop);
+    launch_dq<DEC, 2, 4, 4, 2, kPingPong>(A, M, w, 0, N, g1, g2, y, s, ev.start, ev.stop);
     return hipGetLastError();
   }
-  launch_dq<DEC, 2, 4, 4, 2>(A, M, w, 0, n_main, g1, g2, y, s, ev.start, nullptr);
+  launch_dq<DEC, 2, 4, 4, 2, kPingPong>(A, M, w, 0, n_main, g1, g2, y, s, ev.start, nullptr);
   launch_dq<DEC, 2, 2, 2, 1>(A, M, w, n_main, N - n_main, g1, g2, y, s, nullptr, ev.stop);
   return hipGetLastError();
 }
@@ -537,7 +634,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_mxl_kernel(
   const int wm = wg / WN, wn = wg % WN;
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
+  tile_of(tiles_m, tiles_n, 0, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int rows_m = min(C::BM, M - m0), rows_n = min(C::BN, N - n0);
   const int cb = K / 2, sb = K / 32;

@@ -173,3 +173,40 @@ def test_launch_event_hook_times_the_gemv(bsfp):
     bsfp.time_next_launch(None, None)
     for e in ev:
         rt.hipEventDestroy(e)
+
+
+# One row of x against matrices with few, long rows (16 or 25 steps of 32
+# chunks per row), and the full [5120, 25600] down projection in every base
+# format.
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("N,K", [(1000, 16384), (700, 25600), (5120, 25600)])
+def test_qmv_long_rows(oracle_mod, bsfp, mode, N, K):
+    x = S.generic((1, K), 1.0, seed=470, stream=K)
+    w = S.generic((N, K), 0.02, seed=471 + mode, stream=N)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_onehot_activations_long_rows(oracle_mod, bsfp, mode):
+    """x = e_j with K = 8192 (8 steps per row), N = 77: y[n] = bf16(w_hat[n, j])
+    exactly, for j at both ends of several steps."""
+    o = oracle_mod
+    K, N = 8192, 77
+    w = S.generic((N, K), 0.02, seed=480 + mode)
+    qo = o.quantize(mode, w, use_global=False) if mode == 2 else o.quantize(mode, w)
+    B = o.dequant_exact(qo)
+    for j in (0, 31, 1023, 1024, 2047, 2048, 3100, K - 1025, K - 1):
+        x = np.zeros((1, K), np.uint16)
+        x[0, j] = 0x3F80
+        y = o.bf16_to_f32(run_qmv(o, bsfp, x, qo)[0]).astype(np.float64)
+        ref = o.bf16_to_f32(o.bf16_from_f64(B[:, j])).astype(np.float64)
+        assert np.array_equal(y, ref), j
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_qq_decode_long_rows(oracle_mod, bsfp, mode):
+    """The qq decode GEMV (x quantized while staged) with 25 steps per row."""
+    from test_gpu_qmm import check_qq
+    x = S.generic((1, 25600), 1.0, seed=490, stream=mode)
+    w = S.generic((700, 25600), 0.02, seed=491 + mode)
+    check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
