@@ -189,7 +189,8 @@ __device__ __forceinline__ void load_bfrag_buf(BFrag& f, const rsrc_t& rc, const
 
 // WGM x WGN waves per workgroup, each owning WMT x WNT MFMA tiles of 32 x 32.
 // PP: the ping-pong schedule described at the K loop (8 waves, WGM = 2).
-template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false>
+// NS: LDS stages (3; 2 for the dense 256 x 256 tile, whose stage is 64 KB).
+template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false, int NS = 3>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint16_t* __restrict__ A, const uint32_t* __restrict__ codes,
     const void* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -214,7 +215,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   constexpr int BS_U4 = DENSE ? 0 : BN / 4;       // [BN] scale dwords
   constexpr int BB_U4 = (DEC == DEC_AFFINE) ? BN / 4 : 0;  // [BN] bias dwords
   constexpr int STAGE_U4 = A_U4 + BC_U4 + BS_U4 + BB_U4;
-  __shared__ uint4 smem[3 * STAGE_U4];
+  static_assert(NS == 2 || NS == 3, "two or three LDS stages");
+  static_assert(!PP || NS == 3, "the ping-pong schedule keeps two steps of loads in flight");
+  __shared__ uint4 smem[NS * STAGE_U4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
   // reads, so every step has the same loads in flight.
   const int nsteps = K / 64;
   auto step = [&](int st, int si, int pi) {
-    wait_vmem_le<kStepLoads>();
+    wait_vmem_le<(NS - 2) * kStepLoads>();  // this step's loads have landed
     __syncthreads();
     const uint4* cur = stage(si);
     BFrag b[WNT];
@@ -374,9 +377,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     uint4 a0[WMT], a1[WMT];
     read_a(0, a0);
     read_a(1, a1);
-    // the step's first LDS reads go out before the loads of the step after
-    // next, so their latency overlaps the load issue
-    load_step(min(st + 2, nsteps - 1), stage(pi));
+    // the step's first LDS reads go out before the loads of step st + NS - 1,
+    // so their latency overlaps the load issue
+    load_step(min(st + NS - 1, nsteps - 1), stage(pi));
     mma(0, a0);
     read_a(2, a0);
     mma(1, a1);
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     if (st + 1 < nsteps) pp_step(st + 1, 1, 0);
     if (wm == 0) bar();  // the same number of barriers in both groups
     wait_vmem();  // the surplus loads land before the LDS is released
-  } else {
+  } else if constexpr (NS == 3) {
     load_step(0, stage(0));
     load_step(min(1, nsteps - 1), stage(1));
     int st = 0;
@@ -475,6 +478,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     }
     if (st < nsteps) step(st, 0, 2);
     if (st + 1 < nsteps) step(st + 1, 1, 0);
+    wait_vmem();  // the surplus loads land before the LDS is released
+  } else {
+    // two stages: the loads of step st + 1 go out right after the barrier of
+    // step st, into the stage step st - 1 used
+    load_step(0, stage(0));
+    int st = 0;
+    for (; st + 2 <= nsteps; st += 2) {
+      step(st, 0, 1);
+      step(st + 1, 1, 0);
+    }
+    if (st < nsteps) step(st, 0, 1);
     wait_vmem();  // the surplus loads land before the LDS is released
   }
 
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     }
 }
 
-template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false>
+template <int DEC, int WGM, int WGN, int WMT, int WNT, bool PP = false, int NS = 3>
 void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int n,
                const float* g1, const float* g2, uint16_t* y, hipStream_t s, hipEvent_t ev0,
                hipEvent_t ev1) {
@@ -515,7 +529,7 @@ void launch_dq(const uint16_t* A, int M, const bsfp_qtensor& w, int64_t n0, int 
   const uint32_t* codes = w.codes + n0 * (K / 8);
   const void* scales = reinterpret_cast<const uint8_t*>(w.scales) + n0 * (K / gsz) * sbytes;
   const uint16_t* biases = w.biases ? w.biases + n0 * (K / 64) : nullptr;
-  auto kern = &gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT, PP>;
+  auto kern = &gemm_dq_kernel<DEC, WGM, WGN, WMT, WNT, PP, NS>;
   const dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
   if (ev0 || ev1)
     hipExtLaunchKernelGGL(kern, grid, block, 0u, s, ev0, ev1, 0u, A, codes, scales, biases, g1,
@@ -534,9 +548,24 @@ hipError_t run_dq(const uint16_t* A, int M, const bsfp_qtensor& w, const float* 
 }
 
 // Dense bf16 GEMM y[M, N] = x . B^T on the same kernel (B bf16 [N, K]):
-// 256 x 128 tiles on 8 waves (128 x 32 per wave), three 48 KB LDS stages.
+// 256 x 256 tiles on 8 waves (128 x 64 per wave) with two 64 KB LDS stages
+// from kDenseBigRows rows of x up (5 % faster at M = 4096, 2 % slower at
+// M = 2048), else 256 x 128 tiles (128 x 32 per wave) with three 48 KB
+// stages.
+constexpr int kDenseBigRows = 3072;
+
 hipError_t run_dense(const uint16_t* A, int M, const uint16_t* B, int N, int K, uint16_t* y,
                      hipStream_t s) {
+  if (M >= kDenseBigRows) {
+    constexpr int WGM = 2, WGN = 4, WMT = 4, WNT = 2;
+    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    launch_main(&gemm_dq_kernel<DEC_DENSE, WGM, WGN, WMT, WNT, false, 2>,
+                dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0u, s, A,
+                reinterpret_cast<const uint32_t*>(B), (const void*)nullptr,
+                (const uint16_t*)nullptr, (const float*)nullptr, (const float*)nullptr, M, N, K,
+                y, N, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   constexpr int WGM = 2, WGN = 4, WMT = 4, WNT = 1;
   constexpr int BM = 32 * WMT * WGM, BN = 32 * WNT * WGN;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;

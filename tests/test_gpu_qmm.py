@@ -390,11 +390,12 @@ def test_dense_deterministic(bsfp):
     assert torch.equal(bsfp.qmm_dense(x, q), bsfp.qmm_dense(x, q))
 
 
-@pytest.mark.parametrize("M", [1134, 2048])
+@pytest.mark.parametrize("M", [1134, 2048, 4096])
 def test_dense_prefill_sampled_full_size(oracle_mod, bsfp, M):
     """X[M,5120] . W[25600,5120]^T (NVFP4, global scale) at full size: 64 full
     output rows plus 4096 random outputs against the oracle's dense
-    reference, computed one by one."""
+    reference, computed one by one.  M = 4096 runs the 256 x 256 dense tile
+    with two LDS stages, the others the 256 x 128 tile."""
     o = oracle_mod
     x, w = S.nvfp4_prefill(M=M, N=25600, K=5120, seed=7)
     qo = o.quantize(2, w)
