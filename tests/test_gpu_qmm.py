@@ -237,23 +237,23 @@ def test_nvfp4_prefill_weight_only_sampled_full_size(oracle_mod, bsfp, M):
 
 # 2048 rows x 8448 columns make 8 x 33 = 264 tiles of 256 x 256: on 256 CUs
 # one whole round plus 8 tiles, so the first 8192 columns run on the big
-# tiles and the last 256 on the second launch's 128 x 64 tiles.  K = 128
-# keeps the full oracle product small.
-TAIL_SPLIT = (2048, 8448, 128)
+# tiles and the last 256 on the second launch's 128 x 64 tiles.  A small K
+# (2 and 3 steps of 64) keeps the full oracle product small.
+TAIL_SPLIT = [(2048, 8448, 128), (2048, 8448, 192)]
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
-def test_weight_only_tail_split_full(oracle_mod, bsfp, mode):
-    M, N, K = TAIL_SPLIT
-    x = S.generic((M, K), 1.0, seed=1700 + mode)
-    w = S.generic((N, K), 0.02, seed=1710 + mode)
+@pytest.mark.parametrize("M,N,K", TAIL_SPLIT)
+def test_weight_only_tail_split_full(oracle_mod, bsfp, mode, M, N, K):
+    x = S.generic((M, K), 1.0, seed=1700 + mode, stream=K)
+    w = S.generic((N, K), 0.02, seed=1710 + mode, stream=K)
     check_wonly(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
 
 
-def test_qq_nvfp4_tail_split_full(oracle_mod, bsfp):
-    M, N, K = TAIL_SPLIT
-    x = S.generic((M, K), 0.02, seed=1720)
-    w = S.generic((N, K), 0.02, seed=1721)
+@pytest.mark.parametrize("M,N,K", TAIL_SPLIT)
+def test_qq_nvfp4_tail_split_full(oracle_mod, bsfp, M, N, K):
+    x = S.generic((M, K), 0.02, seed=1720, stream=K)
+    w = S.generic((N, K), 0.02, seed=1721, stream=K)
     check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(2, w))
 
 
