@@ -872,12 +872,331 @@ hipError_t by_m_variant(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_
   return launch_fast<FMT, 8, 1, false, false, false>(x, M, w, nullptr, y, NJ, s, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Several rows of x (2 <= M <= 8) on MFMA: v_mfma_f32_16x16x32_bf16 with x as
+// the A operand (rows M..15 zero) and 16 weight rows, dequantized to bf16 in
+// registers, as the B operand.  The per-row dot products of the GEMV above
+// read every x value from LDS once per weight chunk and row of x, which makes
+// M = 8 LDS-bound (and x beyond 64 KB takes the sliced fallback); here each
+// wave reads an x fragment once for RBW blocks of 16 weight rows.
+//   Contraction order: lane group g = lane / 16 of both operands holds the
+//   32 elements k = 128 kb + 32 g + 0..31 of its row (A lane (m, g), B lane
+//   (n, g); m, n = lane % 16), and MFMA i of block kb takes their elements
+//   8 i .. 8 i + 7.  So a lane's weights are one 16-byte load, and each
+//   lane's 32 elements are one MXFP4 group, two NVFP4 blocks, or half an
+//   affine group of 64 (lane groups 0, 1 and 2, 3 hold its two groups).
+//   MXFP4: the E8M0 scale goes into the E2M1 -> bf16 converter (exact).
+//   NVFP4: E2M1 * E4M3 formed in fp32 and packed to bf16 (exact: at most 6
+//     significant bits); the global scale multiplies the fp32 sums.
+//   affine: the MFMAs run on the exact integer codes q, once with the x of
+//     lane groups 0, 1 and once with those of 2, 3 (the others zeroed), and
+//     on a block of ones for the sums of x in the output layout; each group
+//     adds s * sum(x q) + b * sum(x) in fp32, the numerics of the GEMV above.
+// Grid: one workgroup per group of 16 * RBW weight rows; its S waves split
+// the K blocks (wave w takes blocks [w * kbw, (w + 1) * kbw)) and add their
+// partial tiles through LDS in wave order.  Loads are raw buffer loads whose
+// descriptors end with x and with the group's rows, so rows past N and
+// rows of x past M read as zeros.
+template <int MODE, int RBW, bool ODD>
+__global__ __launch_bounds__(512) void qmv_mma_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
+    const void* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y,
+    int kbw) {
+  static_assert(MODE == FMT_AFF4_G64 || MODE == FMT_MXFP4 || MODE == FMT_NVFP4,
+                "4-bit base formats");
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr bool AFF = MODE == FMT_AFF4_G64;
+  constexpr int D = 2;  // K blocks per register stage
+  constexpr int P = 2;  // register stages: P - 1 of them load while one computes
+  extern __shared__ f32x4_t red[];  // [S][RBW][64] partial tiles
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int S = blockDim.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RBW;
+  const int rows = (int)min((int64_t)N - n0, (int64_t)16 * RBW);
+  const int rb = K / 2;                       // code bytes per row
+  const int nkb = (K + 127) / 128;            // 128-element blocks
+  const int kb0 = w * kbw, kb1 = min(nkb, kb0 + kbw);
+  const rsrc_t rx = make_rsrc(x, (int64_t)M * K * 2);
+  const rsrc_t rc = make_rsrc(reinterpret_cast<const uint8_t*>(codes) + n0 * rb,
+                              (int64_t)rows * rb);
+  const int srb = AFF ? (K / 64) * 2 : (MODE == FMT_MXFP4 ? K / 32 : K / 16);  // scale bytes per row
+  const rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + n0 * srb,
+                              (int64_t)rows * srb);
+  rsrc_t rbs = rs;
+  if constexpr (AFF)
+    rbs = make_rsrc(reinterpret_cast<const uint8_t*>(biases) + n0 * srb, (int64_t)rows * srb);
+
+  f32x4_t acc[RBW];
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // bf16 ones: the B operand that turns an MFMA into sums of x
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  // in the last block (K % 128 != 0) a lane's elements may end early: it
+  // keeps its first vw 8-element words (K is a multiple of 16 for NVFP4, of
+  // 32 otherwise); the words past the row end read the next row's codes or
+  // zeros and are replaced by zeros below, and so are the scales that go
+  // with them, so that no such value reaches the sums (not even a NaN)
+
+  // a ring of P register stages of D blocks each: the loads of the next
+  // P - 1 stages are in flight while one stage is computed
+  struct Stage {
+    uint4 xa[D][4];
+    uint4 wc[D][RBW];
+    uint32_t sc[D][RBW], bc[D][RBW];
+  };
+  // the loads of blocks kbr .. kbr + D - 1.  Every load is issued, with no
+  // branch around it, so that the compiler's wait counts stay exact and the
+  // compute of one stage waits for that stage's loads alone (a load skipped
+  // on some path makes it wait for all of them).  Blocks past kb1 take an
+  // offset past every descriptor's end: zeros, no memory traffic.
+  constexpr int kDead = 0x7FFFFF00;
+  auto load = [&](Stage& st, int kbr) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kb = kbr + d;
+      const bool live = kb < kb1;
+      // x[m, 128 kb + 32 g + 8 i ..]: 64 contiguous bytes per lane
+      const int xo = live ? c * K * 2 + (128 * kb + 32 * g) * 2 : kDead;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.xa[d][i] = buffer_load_u128(rx, xo + 16 * i, 0);
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        const int row = 16 * r + c;
+        st.wc[d][r] = buffer_load_u128(rc, live ? row * rb + 64 * kb + 16 * g : kDead, 0);
+        if constexpr (AFF) {  // both groups of the block: scales, then biases
+          const int so = live ? row * srb + 4 * kb : kDead;
+          if constexpr (!ODD) {  // 4-byte aligned: one load per array
+            st.sc[d][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
+            st.bc[d][r] = __builtin_amdgcn_raw_buffer_load_b32(rbs, so, 0, 0);
+          } else {  // an odd number of groups per row (K % 128 == 64)
+            st.sc[d][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0) |
+                          (__builtin_amdgcn_raw_buffer_load_b16(rs, so + 2, 0, 0) << 16);
+            st.bc[d][r] = __builtin_amdgcn_raw_buffer_load_b16(rbs, so, 0, 0) |
+                          (__builtin_amdgcn_raw_buffer_load_b16(rbs, so + 2, 0, 0) << 16);
+          }
+        } else if constexpr (MODE == FMT_MXFP4) {  // the E8M0 byte of chunk 4 kb + g
+          st.sc[d][r] =
+              __builtin_amdgcn_raw_buffer_load_b8(rs, live ? row * srb + 4 * kb + g : kDead, 0, 0);
+        } else if constexpr (!ODD) {  // the E4M3 bytes of blocks 8 kb + 2 g, 8 kb + 2 g + 1
+          st.sc[d][r] = __builtin_amdgcn_raw_buffer_load_b16(
+              rs, live ? row * srb + 8 * kb + 2 * g : kDead, 0, 0);
+        } else {  // odd bytes per row (K % 32 == 16): the pair may be unaligned
+          const int o = live ? row * srb + 8 * kb + 2 * g : kDead;
+          st.sc[d][r] = __builtin_amdgcn_raw_buffer_load_b8(rs, o, 0, 0) |
+                        (__builtin_amdgcn_raw_buffer_load_b8(rs, o + 1, 0, 0) << 8);
+        }
+      }
+    }
+  };
+  auto compute = [&](const Stage& st, int kbr) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kb = kbr + d;
+      if (kb >= kb1) break;
+      const int vw = min(4, max(0, (K - 128 * kb - 32 * g) >> 3));
+      float sf[RBW][2];
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        if constexpr (MODE == FMT_MXFP4) {
+          // the converter reads the exponent of this float
+          sf[r][0] = vw > 0 ? __uint_as_float((st.sc[d][r] & 0xFFu) << 23) : 1.0f;
+        } else if constexpr (MODE == FMT_NVFP4) {
+          const f32x2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.sc[d][r], 1.0f, false);
+          sf[r][0] = vw > 0 ? sp[0] : 0.0f;
+          sf[r][1] = vw > 2 ? sp[1] : 0.0f;
+        }
+      }
+      f32x4_t xs0 = {0.0f, 0.0f, 0.0f, 0.0f}, xs1 = xs0;
+      f32x4_t dq0[RBW], dq1[RBW];
+      if constexpr (AFF) {
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) dq0[r] = dq1[r] = xs0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 xv = i < vw ? st.xa[d][i] : zero4;
+        if constexpr (AFF) {
+          // groups 2 kb (lane groups 0, 1) and 2 kb + 1 (lane groups 2, 3)
+          const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, g < 2 ? xv : zero4);
+          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, g < 2 ? zero4 : xv);
+          xs0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, ones), xs0,
+                                                        0, 0, 0);
+          xs1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, ones), xs1,
+                                                        0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < RBW; ++r) {
+            const uint4 wv = st.wc[d][r];
+            const uint32_t wd =
+                i >= vw ? 0u : i == 0 ? wv.x : i == 1 ? wv.y : i == 2 ? wv.z : wv.w;
+            // exact integer codes q (E4M3 byte trick)
+            const uint32_t t = wd & 0x0F0F0F0Fu, u = (wd >> 4) & 0x0F0F0F0Fu;
+            const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, false);  // q0, q2
+            const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 512.0f, true);   // q4, q6
+            const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, false);  // q1, q3
+            const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, 512.0f, true);   // q5, q7
+            uint4 bv;
+            bv.x = pack_bf16x2(p0.x, p2.x);
+            bv.y = pack_bf16x2(p0.y, p2.y);
+            bv.z = pack_bf16x2(p1.x, p3.x);
+            bv.w = pack_bf16x2(p1.y, p3.y);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
+            dq0[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, dq0[r], 0, 0, 0);
+            dq1[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, dq1[r], 0, 0, 0);
+          }
+        } else {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xv);
+#pragma unroll
+          for (int r = 0; r < RBW; ++r) {
+            const uint4 wv = st.wc[d][r];
+            const uint32_t wd =
+                i >= vw ? 0u : i == 0 ? wv.x : i == 1 ? wv.y : i == 2 ? wv.z : wv.w;
+            uint4 bv;
+            if constexpr (MODE == FMT_MXFP4) {
+              const float sce = sf[r][0];
+              bv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sce, 0));
+              bv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sce, 1));
+              bv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sce, 2));
+              bv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sce, 3));
+            } else {
+              // words 0, 1 lie in the lane's first NVFP4 block, 2, 3 in its second
+              const float f = sf[r][i >> 1];
+              const f32x2_t q0 = e2m1x2_to_f32x2<0>(wd), q1 = e2m1x2_to_f32x2<1>(wd);
+              const f32x2_t q2 = e2m1x2_to_f32x2<2>(wd), q3 = e2m1x2_to_f32x2<3>(wd);
+              bv.x = pack_bf16x2(q0.x * f, q0.y * f);
+              bv.y = pack_bf16x2(q1.x * f, q1.y * f);
+              bv.z = pack_bf16x2(q2.x * f, q2.y * f);
+              bv.w = pack_bf16x2(q3.x * f, q3.y * f);
+            }
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bv),
+                                                             acc[r], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (AFF) {
+        // per group: s * sum(x q) + b * sum(x), in fp32 (the output lane's
+        // column n = c is this lane's weight row)
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) {
+          // group 2 kb + 1 is past the row end when K - 128 kb <= 64
+          const bool two = K - 128 * kb > 64;
+          const float s0 = __uint_as_float(st.sc[d][r] << 16);
+          const float s1 = two ? __uint_as_float(st.sc[d][r] & 0xFFFF0000u) : 0.0f;
+          const float b0 = __uint_as_float(st.bc[d][r] << 16);
+          const float b1 = two ? __uint_as_float(st.bc[d][r] & 0xFFFF0000u) : 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float a = acc[r][j];
+            a = __builtin_fmaf(s0, dq0[r][j], a);
+            a = __builtin_fmaf(b0, xs0[j], a);
+            a = __builtin_fmaf(s1, dq1[r][j], a);
+            a = __builtin_fmaf(b1, xs1[j], a);
+            acc[r][j] = a;
+          }
+        }
+      }
+    }
+  };
+  Stage ring[P];
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u) load(ring[u], kb0 + u * D);
+  for (int kbr = kb0; kbr < kb1; kbr += P * D) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      load(ring[(u + P - 1) % P], kbr + (u + P - 1) * D);
+      compute(ring[u], kbr + u * D);
+    }
+  }
+
+  // the S partial tiles, added in wave order by the first RBW waves
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) red[(w * RBW + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  if (w >= RBW) return;
+  const int r = w;
+  f32x4_t v = red[r * 64 + lane];
+  for (int q = 1; q < S; ++q) {
+    const f32x4_t o = red[(q * RBW + r) * 64 + lane];
+    v[0] += o[0];
+    v[1] += o[1];
+    v[2] += o[2];
+    v[3] += o[3];
+  }
+  const float gs = ((MODE == FMT_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
+  // output layout: lane (n = lane % 16, g) holds rows m = 4 g .. 4 g + 3
+  const int64_t n = n0 + 16 * r + c;
+  if (n < N) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * g + j;
+      if (m < M) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(v[j] * gs);
+    }
+  }
+}
+
+// Launch shape of qmv_mma_kernel: RBW blocks of 16 rows per workgroup (two
+// for tall matrices, so that x is read once per 32 rows), and up to 8 waves
+// per workgroup splitting K, enough to put about 8 waves on every CU.
+template <int MODE>
+hipError_t launch_mma(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
+                      uint16_t* y, hipStream_t s) {
+  const int64_t N = w.rows;
+  const int K = (int)w.cols;
+  const int nkb = (K + 127) / 128;
+  const int want = 8 * device_cu_count();
+  auto go = [&](auto rbw_c, auto odd_c) {
+    constexpr int RBW = decltype(rbw_c)::value;
+    constexpr bool ODD = decltype(odd_c)::value;
+    const int64_t groups = (N + 16 * RBW - 1) / (16 * RBW);
+    int S = (int)std::min<int64_t>(8, std::max<int64_t>(1, (want + groups - 1) / groups));
+    S = std::min(S, nkb);
+    const int kbw = (nkb + S - 1) / S;
+    S = (nkb + kbw - 1) / kbw;
+    const size_t lds = (size_t)S * RBW * 64 * 16;
+    launch_main(&qmv_mma_kernel<MODE, RBW, ODD>, dim3((unsigned)groups), dim3(64 * S), (uint32_t)lds, s,
+                x, M, K, (int)N, w.codes, w.scales, w.biases, w.global_scale, g2, y, kbw);
+    return hipGetLastError();
+  };
+  using one = std::integral_constant<int, 1>;
+  using two = std::integral_constant<int, 2>;
+  using odd = std::integral_constant<bool, true>;
+  using even = std::integral_constant<bool, false>;
+  // rows whose scale pairs are not aligned for one wider load: NVFP4 with
+  // K % 32 == 16 (an odd number of scale bytes), affine with K % 128 == 64
+  // (an odd number of groups)
+  if constexpr (MODE == FMT_NVFP4 || MODE == FMT_AFF4_G64) {
+    const bool odd_row = MODE == FMT_NVFP4 ? (K / 16) % 2 != 0 : (K / 64) % 2 != 0;
+    if (odd_row) return N >= 16384 ? go(two{}, odd{}) : go(one{}, odd{});
+  }
+  return N >= 16384 ? go(two{}, even{}) : go(one{}, even{});
+}
+
+// When the GEMV runs on MFMA (qmv_mma_kernel), by measurement on the
+// [25600, 5120], [5120, 25600], [5760, 2880] and [4096, 4096] shapes:
+// - x too large for the one LDS copy of the kernels below (which then walk
+//   K in slices): from 4 rows of x on, 1.1-3x faster;
+// - x in LDS: from 5 rows on, for matrices under 2^26 weights (1.2-1.4x
+//   faster); on larger ones the LDS kernels stream the weights faster up to
+//   the 64 KB limit of x (their loads touch fewer cache lines per
+//   instruction than the MFMA operand layout allows).
+constexpr int kMmaMinRows = 5;
+constexpr int64_t kMmaLargeWeights = int64_t(1) << 26;
+
 template <int MODE, bool QX = false>
 hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2, uint16_t* y,
                 hipStream_t s, int qx_amax = 0) {
   const int K = (int)w.cols;
   const int NJ = (int)((w.cols / 32 + 31) / 32);
   const bool ragged = (w.cols / 32) % 32 != 0;
+  if constexpr (!QX && (MODE == FMT_AFF4_G64 || MODE == FMT_MXFP4 || MODE == FMT_NVFP4)) {
+    const bool x_lds = fast_ok<MODE>(M, NJ);
+    const bool mma = x_lds ? (M >= kMmaMinRows && w.rows * w.cols < kMmaLargeWeights)
+                           : M >= kMmaMinRows - 1;
+    if (mma && w.cols < (1 << 26) && w.rows < (1 << 30)) return launch_mma<MODE>(x, M, w, g2, y, s);
+  }
   if (fast_ok<MODE>(M, NJ) && w.cols < (1 << 28) && w.rows < (1 << 30)) {
     if (M == 1) {
       // two rows per team once that still gives every CU 8 waves (measured

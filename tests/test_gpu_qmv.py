@@ -61,7 +61,7 @@ def test_qmv_many_blocks_per_wave(oracle_mod, bsfp, mode):
 
 
 def test_nvfp4_k_not_multiple_of_32(oracle_mod, bsfp):
-    for M in (1, 4):
+    for M in (1, 4, 6):
         for K in (16, 48, 16 * 33):
             x = S.generic((M, K), 1.0, seed=K)
             w = S.generic((70, K), 0.02, seed=K + 1)
@@ -210,3 +210,38 @@ def test_qq_decode_long_rows(oracle_mod, bsfp, mode):
     x = S.generic((1, 25600), 1.0, seed=490, stream=mode)
     w = S.generic((700, 25600), 0.02, seed=491 + mode)
     check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+# Where x exceeds the 64 KB LDS copy of the other kernels (from 4 rows of x),
+# and from 5 rows on matrices under 2^26 weights, the GEMV runs on MFMA (x as
+# the A operand, 16 weight rows dequantized in registers as the B operand).
+# At hidden 5120 eight rows of x (80 KB) take the MFMA kernel and six stay
+# with the LDS kernels; at K = 25600 all three counts take the MFMA kernel.
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("M", [4, 6, 8])
+def test_qmv_rows_decode_shapes(oracle_mod, bsfp, mode, M):
+    for N, K, which in ((25600, 5120, 0), (5120, 25600, 1)):
+        x = S.generic((M, K), 1.0, seed=495 + M, stream=K)
+        w = S.generic((N, K), 0.02, seed=496 + mode, stream=which)
+        check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_onehot_activations_rows(oracle_mod, bsfp, mode):
+    """Eight rows of x, row m = e_{j_m}: y[m, n] = bf16(w_hat[n, j_m]) on the
+    MFMA GEMV (exact for MXFP4 and NVFP4 without a global scale; one bf16 step
+    for affine), for j at chunk and block edges and past 128-element blocks."""
+    o = oracle_mod
+    K, N, M = 64 * 13, 70, 8
+    w = S.generic((N, K), 0.02, seed=497 + mode)
+    qo = o.quantize(mode, w, use_global=False) if mode == 2 else o.quantize(mode, w)
+    B = o.dequant_exact(qo)
+    j = np.array([0, 7, 8, 31, 32, 127, 128, K - 1])
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), j] = 0x3F80
+    y = o.bf16_to_f32(run_qmv(o, bsfp, x, qo)).astype(np.float64)
+    ref = o.bf16_to_f32(o.bf16_from_f64(B[:, j].T)).astype(np.float64)
+    if mode == 0:
+        assert np.all(np.abs(y - ref) <= np.abs(ref) * 2 ** -7 + 1e-30)
+    else:
+        assert np.array_equal(y, ref)
