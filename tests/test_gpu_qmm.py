@@ -98,7 +98,7 @@ def test_qq_nvfp4_activation_outliers(oracle_mod, bsfp):
     check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(2, w))
 
 
-@pytest.mark.parametrize("M", [32, 512, 2048])
+@pytest.mark.parametrize("M", [32, 200, 512, 2048])
 def test_mxfp4_config_qq_full(oracle_mod, bsfp, M):
     w = S.mxfp4_weights()
     x = S.mxfp4_activations(M)
@@ -112,11 +112,12 @@ def test_mxfp4_config_weight_only_full(oracle_mod, bsfp, M):
     check_wonly(oracle_mod, bsfp, x, oracle_mod.quantize(1, w))
 
 
-@pytest.mark.parametrize("M", [20, 100])
+@pytest.mark.parametrize("M", [20, 100, 300])
 @pytest.mark.parametrize("K", [384, 704, 768, 2880])
 def test_mxfp4_qq_k_units(oracle_mod, bsfp, M, K):
     """MXFP4 x MXFP4 walks K in units of 256 plus one last unit of 64, 128
-    or 192 (K % 256): every unit size, at tile shapes of both row ranges."""
+    or 192 (K % 256): every unit size, at the tile shapes of all three row
+    ranges (up to 64, up to 256, beyond)."""
     x = S.generic((M, K), 0.02, seed=650 + M, stream=K)
     w = S.generic((300, K), 0.02, seed=651, stream=K)
     check_qq(oracle_mod, bsfp, x, oracle_mod.quantize(1, w))
