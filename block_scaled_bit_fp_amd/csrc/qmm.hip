@@ -147,7 +147,11 @@ __device__ __forceinline__ f32x16_t mfma16(const uint4& a, const Op8& b, const f
 // tiles that share operands share that XCD's L2.  m_major: consecutive
 // logical tiles share an activation row block (the weight column blocks
 // stream past it); otherwise they share a weight column block across the M
-// tiles.
+// tiles, in groups of 4 M tiles when the M tiles come in multiples of 4: an
+// XCD's 32 concurrent tiles are then 4 row blocks x 8 column blocks instead
+// of 8 x 4, and it streams half the activation rows (at M = 2048 the qq GEMM
+// fetches 30 % fewer bytes at the same speed, the dense GEMM runs 3 %
+// faster; at M = 1134, 5 row blocks, the ungrouped order was faster).
 // m_major = 1 from 16 row blocks up (the 16-bit GEMM at M = 4096 read 3 %
 // faster that way; at M = 1134 the weight-column order was faster).
 __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int m_major, int& tm,
@@ -158,6 +162,10 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int m_major, i
   if (m_major) {
     tm = L / tiles_n;
     tn = L % tiles_n;
+  } else if (tiles_m % 4 == 0) {
+    const int grp = L / (4 * tiles_n), within = L - grp * 4 * tiles_n;
+    tm = grp * 4 + (within & 3);
+    tn = within >> 2;
   } else {
     tm = L % tiles_m;
     tn = L / tiles_m;
