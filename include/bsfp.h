@@ -181,7 +181,12 @@ bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
 /*
  * bsfp_qmm_workspace_bytes: device scratch bytes that bsfp_qmm needs for
  * (mode, M, K, act): for BSFP_ACT_SAME, x's codes, scales and (NVFP4) amax
- * and g; 0 for BSFP_ACT_BF16.  Returns 0 for unsupported arguments.
+ * and g; 0 for BSFP_ACT_BF16.  Returns 0 for unsupported arguments.  The
+ * quantized x is the intermediate that QQMatmul::eval_gpu allocates itself
+ * before the GEMM (quantize_input with x's packed codes and scales, and the
+ * NVFP4 scalars of create_nvfp4_scalars: "mlx 0.30.7.3 -> 0.30.7.6",
+ * qqmm.cpp and qqmm_utils.cu); here the caller owns it, so that the library
+ * allocates nothing.
  */
 size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act);
 
