@@ -15,7 +15,10 @@ already resident in HBM:
               random word per element, drawn on the device beforehand)
   qmv_sweep   affine g64 decode GEMV over 64 layers x {gate, up, down}
               ([25600,5120], [25600,5120], [5120,25600]): 192 distinct matrices,
-              14.17 GB of packed weights (more than the 256 MB Infinity Cache)
+              14.17 GB of packed weights (more than the 256 MB Infinity Cache);
+              per layer gate and up, which share x, run as one bsfp_qmv_batch
+              launch and down as one bsfp_qmv launch (128 launches)
+  qmv_sweep_single   the same sweep with one bsfp_qmv launch per matrix (192)
   qmv_mx1 / qmv_mx8   MXFP4 qmv W[5760,2880] at M = 1 and 8: a burst of 32
               calls over 32 distinct weight copies (282 MB, more than the
               Infinity Cache), reported per call (`qmv_fp4_gbs`)
@@ -140,6 +143,11 @@ def main():
             x = x_dec if K == HIDDEN else x_dec_down
             sweep.append((x, q, torch.empty((1, N), dtype=torch.bfloat16, device=dev)))
     sweep_bytes = sum(affine_bytes(q.rows, q.cols) for _, q, _ in sweep)
+    # the same sweep as a decoder runs it: per layer, gate and up (same x) in
+    # one bsfp_qmv_batch launch, then down
+    sweep_layers = [(sweep[3 * l][0], [sweep[3 * l][1], sweep[3 * l + 1][1]],
+                     [sweep[3 * l][2], sweep[3 * l + 1][2]], sweep[3 * l + 2])
+                    for l in range(LAYERS)]
 
     x_mx = {M: to_dev(S.mxfp4_activations(M)) for M in (1, 8, 32, 512)}
     y_mx = {M: torch.empty((M, 5760), dtype=torch.bfloat16, device=dev) for M in (1, 8, 32, 512)}
@@ -210,6 +218,11 @@ def main():
     recording = [False]
 
     def st_qmv_sweep():
+        for x, qs, ys, (xd, qd, yd) in sweep_layers:
+            b.qmv_batch(x, qs, outs=ys)
+            b.qmv(xd, qd, out=yd)
+
+    def st_qmv_sweep_single():  # one launch per matrix
         for x, q, y in sweep:
             b.qmv(x, q, out=y)
 
@@ -316,7 +329,8 @@ def main():
     stages = [("act_quant", st_act_quant), ("act_quant_warm", st_act_quant_warm),
               ("act_quant_sr", st_act_quant_sr),
               ("dequant", st_dequant), ("w_quant", st_w_quant),
-              ("qmv_sweep", st_qmv_sweep), ("qmv_mx1", qmv_mx(1)), ("qmv_mx8", qmv_mx(8)),
+              ("qmv_sweep", st_qmv_sweep), ("qmv_sweep_single", st_qmv_sweep_single),
+              ("qmv_mx1", qmv_mx(1)), ("qmv_mx8", qmv_mx(8)),
               ("qmv_nv1", st_qmv_nv1), ("qq_decode", st_qq_decode)]
     stages += [(f"qmv_{name}", qmv_var(name)) for name in VARIANTS]
     stages += [("qqmm", qq(2048)), ("qqmm_1134", qq(1134)), ("qqmm_4096", qq(4096)),
@@ -379,21 +393,32 @@ def main():
         gbs = sweep_bytes / (ms["qmv_sweep"] * 1e-3) / 1e9
         out["value"] = round(gbs, 1)
         out["qmv_sweep_gbs"] = round(gbs, 1)
-        per_launch = sweep_bytes / len(sweep)
-        launch_ms = ms["qmv_sweep"] / len(sweep)
+        launches = 2 * len(sweep_layers)
+        per_launch = sweep_bytes / launches
+        launch_ms = ms["qmv_sweep"] / launches
         kgbs = per_launch / (launch_ms * 1e-3) / 1e9
+        up_bytes = affine_bytes(INTER, HIDDEN)
         out["roofline"] = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic("qmv_affine_m1", ["qmv.hip"]),
                            "kernel": "qmv_fast_kernel<affine, M=1>",
                            "bytes_per_launch": int(per_launch),
+                           "bytes_per_launch_by_kind": {"gate+up (one qmv_batch launch)":
+                                                        2 * up_bytes,
+                                                        "down": affine_bytes(HIDDEN, INTER)},
                            "launch_us": round(launch_ms * 1e3, 3),
-                           "launches_per_sweep": len(sweep),
-                           "note": "algorithmic bytes of one launch / mean launch duration: "
-                                   "HIP events on the GEMV's stream around the sweep's "
-                                   "back-to-back launches (median over the timed steps) "
-                                   "divided by their number, so the short gaps between "
-                                   "launches count as kernel time"}
+                           "launches_per_sweep": launches,
+                           "note": "per layer, gate and up (which share x) run as one "
+                                   "bsfp_qmv_batch launch and down as one bsfp_qmv launch; "
+                                   "algorithmic bytes per launch (mean over the two kinds) / "
+                                   "mean launch duration: HIP events on the GEMV's stream "
+                                   "around the sweep's back-to-back launches (median over "
+                                   "the timed steps) divided by their number, so the short "
+                                   "gaps between launches count as kernel time"}
+    if "qmv_sweep_single" in ms:
+        gbs1 = sweep_bytes / (ms["qmv_sweep_single"] * 1e-3) / 1e9
+        out["qmv_sweep_single_gbs"] = round(gbs1, 1)
+        out["qmv_sweep_single_launch_us"] = round(ms["qmv_sweep_single"] * 1e3 / len(sweep), 3)
     if "qqmm" in ms:
         flop = 2.0 * 2048 * INTER * HIDDEN
         tfs = flop / (ms["qqmm"] * 1e-3) / 1e12
@@ -480,7 +505,8 @@ def main():
             hbm_row("w_quant", 5760 * 2880 * 2 + 5760 * 2880 // 2 + 5760 * 90
                     + 1024 * 512 * 2 + 1024 * 512 // 2 + 2 * 2 * 1024 * 8),
         "a5 NVFP4 dequantize [4096,5120]": hbm_row("dequant", NX // 2 + NX // 16 + NX * 2),
-        "a6 affine qmv sweep": hbm_row("qmv_sweep", sweep_bytes),
+        "a6 affine qmv sweep (gate+up batched)": hbm_row("qmv_sweep", sweep_bytes),
+        "a6 affine qmv sweep, one launch per matrix": hbm_row("qmv_sweep_single", sweep_bytes),
         "a7 NVFP4 qmv [25600,5120] M=1": hbm_row("qmv_nv1", fp4_bytes(INTER, HIDDEN, 16, 1)),
         "a7 MXFP4 qmv [5760,2880] M=1": hbm_row("qmv_mx1", fp4_bytes(5760, 2880, 32, 1)),
         "a7 MXFP4 qmv [5760,2880] M=8": hbm_row("qmv_mx8", fp4_bytes(5760, 2880, 32, 8)),

@@ -29,11 +29,13 @@ GS_NONE, GS_COMPUTE, GS_GIVEN = 0, 1, 2
 ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
 
-EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv",
+EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv", "bsfp_qmv_batch",
            "bsfp_quantize_sr", "bsfp_qmm_workspace_bytes", "bsfp_qmm",
            "bsfp_qmm_dense_scratch_bytes",
            "bsfp_qmm_dense", "bsfp_qmm_noalloc", "bsfp_time_next_launch", "bsfp_last_error",
            "bsfp_version")
+# most matrices of one bsfp_qmv_batch call (BSFP_QMV_BATCH_MAX)
+QMV_BATCH_MAX = 4
 # bytes of bsfp_qmm_noalloc's static device workspace (BSFP_NOALLOC_WORKSPACE_BYTES)
 NOALLOC_WORKSPACE_BYTES = 32 << 20
 
@@ -71,6 +73,7 @@ def lib():
             "bsfp_quantize_sr": (C.c_int, [P, QP, I32, P, P]),
             "bsfp_dequantize": (C.c_int, [QP, P, P]),
             "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
+            "bsfp_qmv_batch": (C.c_int, [P, I64, C.POINTER(QP), I32, C.POINTER(P), P]),
             "bsfp_qmm_workspace_bytes": (C.c_size_t, [I32, I64, I64, I32]),
             "bsfp_qmm": (C.c_int, [P, I64, QP, I32, P, C.c_size_t, P, P]),
             "bsfp_qmm_dense_scratch_bytes": (C.c_size_t, [I64, I64]),
@@ -275,6 +278,30 @@ def qmv(x: torch.Tensor, w: QuantizedTensor, out: Optional[torch.Tensor] = None)
     d = w.desc()
     _check(lib().bsfp_qmv(_ptr(x2), M, C.byref(d), _ptr(out), _stream()))
     return out
+
+
+def qmv_batch(x: torch.Tensor, ws, outs=None):
+    """[x . dq(W_i)^T for W_i in ws]: the decode GEMV of several matrices that
+    share x, K and the format (bsfp_qmv_batch: one launch where the kernels
+    allow).  outs: optional list of bf16 [M, W_i.rows] outputs."""
+    ws = list(ws)
+    if not 1 <= len(ws) <= QMV_BATCH_MAX:
+        raise ValueError(f"qmv_batch takes 1..{QMV_BATCH_MAX} matrices, got {len(ws)}")
+    x2 = _as_2d_bf16(x)
+    M = x2.shape[0]
+    for w in ws:
+        if x2.shape[1] != w.cols:
+            raise ValueError(f"x has K={x2.shape[1]}, W has K={w.cols}")
+    if outs is None:
+        outs = [None] * len(ws)
+    if len(outs) != len(ws):
+        raise ValueError("qmv_batch needs one output per matrix")
+    outs = [_out_bf16(o, (M, w.rows), x.device) for o, w in zip(outs, ws)]
+    descs = [w.desc() for w in ws]
+    darr = (C.POINTER(QTensorDesc) * len(ws))(*[C.pointer(d) for d in descs])
+    yarr = (C.c_void_p * len(ws))(*[_ptr(o) for o in outs])
+    _check(lib().bsfp_qmv_batch(_ptr(x2), M, darr, len(ws), yarr, _stream()))
+    return outs
 
 
 def qmm_workspace_bytes(mode: int, M: int, K: int, act: str = "bf16") -> int:

@@ -280,6 +280,38 @@ bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w, uint16
   return device_status(launch_qmv(x, (int)M, *w, y, (hipStream_t)stream), "bsfp_qmv");
 }
 
+bsfp_status bsfp_qmv_batch(const uint16_t* x, int64_t M, const bsfp_qtensor* const* w,
+                           int32_t count, uint16_t* const* y, bsfp_stream stream) {
+  if (count < 1 || count > BSFP_QMV_BATCH_MAX)
+    return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: count = %d outside 1..%d", (int)count,
+                BSFP_QMV_BATCH_MAX);
+  if (!w || !y) return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: null descriptor or output array");
+  for (int i = 0; i < count; ++i)
+    if (!w[i]) return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: descriptor %d is null", i);
+  for (int i = 0; i < count; ++i) {
+    bsfp_status st = check_qtensor(w[i], "bsfp_qmv_batch");
+    if (st != BSFP_OK) return st;
+    if (w[i]->mode != w[0]->mode || w[i]->bits != w[0]->bits ||
+        w[i]->group_size != w[0]->group_size || w[i]->cols != w[0]->cols)
+      return fail(BSFP_ERR_ARG,
+                  "bsfp_qmv_batch: matrix %d differs from matrix 0 in format or K", i);
+    if (w[i]->rows > 0 && (!y[i] || !aligned16(y[i])))
+      return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: output %d is null or not 16-byte aligned", i);
+  }
+  if (M < 1 || M > 8)
+    return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: M = %lld outside 1..8", (long long)M);
+  if (w[0]->cols == 0) return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: K must be positive");
+  if (!x || !aligned16(x))
+    return fail(BSFP_ERR_ARG, "bsfp_qmv_batch: x is null or not 16-byte aligned");
+  if (is_variant(w[0]) && !qmv_variant_supported((int)M, *w[0]))
+    return fail(BSFP_ERR_UNSUPPORTED,
+                "bsfp_qmv_batch: %s %d-bit group %d needs x of at most 64 KB and K < 2^28 "
+                "(M = %lld, K = %lld)", mode_name(w[0]->mode), (int)w[0]->bits,
+                (int)w[0]->group_size, (long long)M, (long long)w[0]->cols);
+  return device_status(launch_qmv_batch(x, (int)M, w, y, count, (hipStream_t)stream),
+                       "bsfp_qmv_batch");
+}
+
 size_t bsfp_qmm_workspace_bytes(int32_t mode, int64_t M, int64_t K, int32_t act) {
   if (mode < BSFP_AFFINE || mode > BSFP_NVFP4 || M < 0 || K < 0) return 0;
   if (act != BSFP_ACT_BF16 && act != BSFP_ACT_SAME) return 0;

@@ -77,6 +77,11 @@ hipError_t launch_dequantize(const bsfp_qtensor& q, uint16_t* out, hipStream_t s
 // path passes g_x there).
 hipError_t launch_qmv(const uint16_t* x, int M, const bsfp_qtensor& w, uint16_t* y,
                       hipStream_t s, const float* g2 = nullptr);
+// The GEMV of `count` (<= 4) matrices that share x, K and the format, in one
+// launch where the kernels allow (one row of x, base formats), else one
+// launch per matrix.
+hipError_t launch_qmv_batch(const uint16_t* x, int M, const bsfp_qtensor* const* ws,
+                            uint16_t* const* ys, int count, hipStream_t s);
 // qq decode GEMV: x is quantized with w's format (NVFP4: global scale from
 // x's amax when w has one) while the GEMV stages it, and the products run on
 // its exact dequantization, with alpha = g_x * g_w on the output.  Applies

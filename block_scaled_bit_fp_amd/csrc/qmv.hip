@@ -393,6 +393,37 @@ int slds_wave_bytes(int R, int K) {
   return 2 * win * 1024 * (fmt_affine(MODE) ? 2 : 1);
 }
 
+// The weight matrices of one launch of the fast kernel.  Several matrices
+// that share x, K and the format (a decoder's gate and up projections) run
+// as one launch: their blocks of 2R rows are numbered one matrix after the
+// other (matrix i owns blocks bstart[i] ..), each block reads its own
+// matrix and writes its own y, scaled by its own global scale.  A single
+// matrix is count = 1.  NM slots; the kernel arguments stay as small as
+// a single matrix's for NM = 1.
+constexpr int kQmvMats = 4;
+template <int NM>
+struct QmvMats {
+  const uint8_t* codes[NM];
+  const uint8_t* scales[NM];
+  const uint8_t* biases[NM];
+  const float* gscale[NM];  // NVFP4 global scale (NULL: 1)
+  uint16_t* y[NM];
+  int rows[NM];
+  int bstart[NM];
+  int count;
+};
+
+// a[i] for a wave-uniform i < NM, by selects over constant indices (a
+// dynamic index into a kernel-argument array would copy it to scratch
+// memory); NM = 1 reads a[0] alone
+template <int NM, class T, int L>
+__device__ __forceinline__ T pick(const T (&a)[L], int i) {
+  T v = a[0];
+#pragma unroll
+  for (int j = 1; j < NM; ++j) v = (i == j) ? a[j] : v;
+  return v;
+}
+
 // MAXM: compile-time bound on M.  R: rows per team per block.
 // RAGGED: the row length in chunks is not a multiple of 32, so some lanes
 //   have no chunk in the last step; their scale and bias are forced to zero
@@ -416,12 +447,12 @@ int slds_wave_bytes(int R, int K) {
 // qx_amax set, every workgroup takes the global activation scale
 // g_x = amax(x) / 2688 over the whole x it stages and folds it into the
 // output scale (without it, g_x = 1).
-template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
+// NM: matrix slots of the launch (1 for one matrix; the code for the
+// matrix list is compiled only where it is used).
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX, int NM = 1>
 __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int N, const uint32_t* __restrict__ codes,
-    const void* __restrict__ scales, const uint16_t* __restrict__ biases,
-    const float* __restrict__ gptr, const float* __restrict__ g2ptr, uint16_t* __restrict__ y,
-    int NJ, int nblocks, int qx_amax) {
+    const uint16_t* __restrict__ x, int M, int K, const QmvMats<NM> mats,
+    const float* __restrict__ g2ptr, int NJ, int nblocks, int qx_amax) {
   static_assert(!QX || MODE == FMT_MXFP4 || MODE == FMT_NVFP4,
                 "qq needs a 4-bit float format");
   static_assert(!(SLDS && RAGGED), "staged scales need whole 32-chunk steps");
@@ -452,7 +483,12 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   const int nb_wg = nblocks > wg ? (nblocks - wg + G - 1) / G : 0;
   const int passes = wave_in_wg < nb_wg ? (nb_wg - wave_in_wg + wpg - 1) / wpg : 0;
   const int steps = passes * NJ;
-  float g = ((MODE == BSFP_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
+  // output scale factors: a block's is ((its matrix's NVFP4 global scale)
+  // * g2) * gq, in this order (gq: the qq decode's activation scale)
+  const float g2v = g2ptr ? *g2ptr : 1.0f;
+  // one matrix: its global scale, read once; a matrix list reads its
+  // block's matrix's at the block's end
+  const float gw0 = (MODE == BSFP_NVFP4 && mats.gscale[0]) ? *mats.gscale[0] : 1.0f;
 
   // this wave's scale areas (SLDS): two block buffers, each nsl KB of
   // [2R rows][srb] scales, then nsl KB of biases
@@ -473,16 +509,23 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   }
 
   rsrc_t rc, rs, rbs;
-  auto block_row0 = [&](int p) -> int64_t {
-    return ((int64_t)(p * wpg + wave_in_wg) * G + wg) * (2 * R);
+  // pass p's block: its matrix and first row there
+  auto block_of = [&](int p, int& mi, int64_t& row0) {
+    const int gb = (p * wpg + wave_in_wg) * G + wg;
+    mi = 0;
+#pragma unroll
+    for (int j = 1; j < NM; ++j)
+      if (j < mats.count && gb >= mats.bstart[j]) mi = j;
+    row0 = (int64_t)(gb - pick<NM>(mats.bstart, mi)) * (2 * R);
   };
   auto set_block = [&](int p) {
-    const int64_t row0 = block_row0(p);
-    const int64_t rows = min((int64_t)N - row0, (int64_t)(2 * R));
-    rc = make_rsrc(reinterpret_cast<const uint8_t*>(codes) + row0 * rb, rows * rb);
-    rs = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + row0 * srb, rows * srb);
-    if constexpr (AFF)
-      rbs = make_rsrc(reinterpret_cast<const uint8_t*>(biases) + row0 * srb, rows * srb);
+    int mi;
+    int64_t row0;
+    block_of(p, mi, row0);
+    const int64_t rows = min((int64_t)pick<NM>(mats.rows, mi) - row0, (int64_t)(2 * R));
+    rc = make_rsrc(pick<NM>(mats.codes, mi) + row0 * rb, rows * rb);
+    rs = make_rsrc(pick<NM>(mats.scales, mi) + row0 * srb, rows * srb);
+    if constexpr (AFF) rbs = make_rsrc(pick<NM>(mats.biases, mi) + row0 * srb, rows * srb);
   };
   constexpr int SL = (MODE == BSFP_NVFP4) ? 4 : 2;
   // fetch step j of the current block; `real` is false for the refills past
@@ -538,9 +581,9 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
   if (steps > 0) {
     set_block(0);
   } else {
-    rc = make_rsrc(codes, 0);
-    rs = make_rsrc(scales, 0);
-    if constexpr (AFF) rbs = make_rsrc(biases, 0);
+    rc = make_rsrc(mats.codes[0], 0);
+    rs = make_rsrc(mats.scales[0], 0);
+    if constexpr (AFF) rbs = make_rsrc(mats.biases[0], 0);
   }
 #pragma unroll
   for (int u = 0; u < PJ; ++u) {
@@ -571,7 +614,6 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
       for (int w2 = 1; w2 < wpg; ++w2) a = fmaxf(a, red[w2]);
       __syncthreads();
       gq = a / 2688.0f;
-      g *= gq;
     }
   }
   stage_x_store<AFF, AFF && BITS == 4, fast_xu<MODE, MAXM>(), QX ? MODE : -1>(M, NJ, xr, xp, xs, gq);
@@ -711,7 +753,17 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
           }
         }
         if (jc == NJ - 1) {  // the block's rows are complete
-          const int64_t row0 = block_row0(pc);
+          int mi;
+          int64_t row0;
+          block_of(pc, mi, row0);
+          const int64_t N = pick<NM>(mats.rows, mi);
+          uint16_t* const y = pick<NM>(mats.y, mi);
+          float gwi = gw0;
+          if constexpr (NM > 1) {
+            const float* const gs_i = pick<NM>(mats.gscale, mi);
+            gwi = (MODE == BSFP_NVFP4 && gs_i) ? *gs_i : 1.0f;
+          }
+          const float gb = (gwi * g2v) * gq;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const int64_t row = row0 + 2 * r + h;
@@ -719,7 +771,7 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
             for (int m = 0; m < MAXM; ++m) {
               if (MAXM > 1 && m >= M) break;
               const float v = dpp_sum32(acc[r][m]);
-              if (lt == 0 && row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16(v * g);
+              if (lt == 0 && row < N) y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16(v * gb);
               acc[r][m] = 0.0f;
             }
           }
@@ -777,12 +829,14 @@ struct FastShape {
   size_t lds;
 };
 
+// nblocks: the launch's blocks of 2R rows (a matrix list's, summed over its
+// matrices), or -1 for one matrix of N rows.
 template <int MODE, int MAXM, int R, bool SLDS>
-FastShape fast_shape(int M, int K, int NJ, int64_t N) {
+FastShape fast_shape(int M, int K, int NJ, int64_t N, int64_t nblocks = -1) {
   constexpr int kMaxW = fast_threads<MODE, MAXM>() / 64, kXu = fast_xu<MODE, MAXM>();
   constexpr int kPerCu = 1024 / fast_threads<MODE, MAXM>();  // workgroups per CU
   const int cus = device_cu_count();
-  const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
+  if (nblocks < 0) nblocks = (N + 2 * R - 1) / (2 * R);
   const int units = M * NJ * 128;
   const int min_wpg = std::max(1, (units + kXu * 64 - 1) / (kXu * 64));
   const int64_t grid = std::min<int64_t>((int64_t)kPerCu * cus, nblocks);
@@ -796,13 +850,37 @@ FastShape fast_shape(int M, int K, int NJ, int64_t N) {
   return FastShape{(int)grid, wpg, lds};
 }
 
-template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
-hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
-                       uint16_t* y, int NJ, hipStream_t s, int qx_amax) {
-  const int64_t N = w.rows;
-  const int K = (int)w.cols;
-  const FastShape sh = fast_shape<MODE, MAXM, R, SLDS>(M, K, NJ, N);
-  const int64_t nblocks = (N + 2 * R - 1) / (2 * R);
+// A matrix list of `count` matrices that share x, K and the format; returns
+// its number of blocks of 2R rows.
+template <int NM>
+int64_t fill_mats(QmvMats<NM>& m, const bsfp_qtensor* const* ws, uint16_t* const* ys,
+                  int count, int R) {
+  m = QmvMats<NM>{};
+  int64_t nb = 0;
+  for (int i = 0; i < count; ++i) {
+    m.codes[i] = reinterpret_cast<const uint8_t*>(ws[i]->codes);
+    m.scales[i] = reinterpret_cast<const uint8_t*>(ws[i]->scales);
+    m.biases[i] = reinterpret_cast<const uint8_t*>(ws[i]->biases);
+    m.gscale[i] = ws[i]->global_scale;
+    m.y[i] = ys[i];
+    m.rows[i] = (int)ws[i]->rows;
+    m.bstart[i] = (int)nb;
+    nb += (ws[i]->rows + 2 * R - 1) / (2 * R);
+  }
+  m.count = count;
+  return nb;
+}
+
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX, int NM = 1>
+hipError_t launch_fast_mats(const uint16_t* x, int M, const bsfp_qtensor* const* ws,
+                            uint16_t* const* ys, int count, const float* g2, int NJ,
+                            hipStream_t s, int qx_amax) {
+  const int K = (int)ws[0]->cols;
+  QmvMats<NM> mats;
+  const int64_t nblocks = fill_mats(mats, ws, ys, count, R);
+  int64_t N = 0;
+  for (int i = 0; i < count; ++i) N += ws[i]->rows;
+  const FastShape sh = fast_shape<MODE, MAXM, R, SLDS>(M, K, NJ, N, nblocks);
   // opt in to the large LDS allocation (160 KB on gfx950), once per device
   // and size
   static std::atomic<size_t> lds_granted[64];
@@ -810,15 +888,23 @@ hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const fl
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (sh.lds > 64 * 1024 && sh.lds > lds_granted[dev].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX>),
+        reinterpret_cast<const void*>(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX, NM>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
     if (e != hipSuccess) return e;
     lds_granted[dev].store(sh.lds, std::memory_order_relaxed);
   }
-  launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX>, dim3((unsigned)sh.grid),
-                     dim3(64 * sh.wpg), sh.lds, s, x, M, K, (int)N, w.codes, w.scales,
-                     w.biases, w.global_scale, g2, y, NJ, (int)nblocks, qx_amax);
+  launch_main(&qmv_fast_kernel<MODE, MAXM, R, RAGGED, SLDS, QX, NM>, dim3((unsigned)sh.grid),
+                     dim3(64 * sh.wpg), sh.lds, s, x, M, K, mats, g2, NJ, (int)nblocks,
+                     qx_amax);
   return hipGetLastError();
+}
+
+template <int MODE, int MAXM, int R, bool RAGGED, bool SLDS, bool QX>
+hipError_t launch_fast(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
+                       uint16_t* y, int NJ, hipStream_t s, int qx_amax) {
+  const bsfp_qtensor* ws[1] = {&w};
+  uint16_t* ys[1] = {y};
+  return launch_fast_mats<MODE, MAXM, R, RAGGED, SLDS, QX>(x, M, ws, ys, 1, g2, NJ, s, qx_amax);
 }
 
 // The staged x (XU units per thread) is limited to 64 KB; the per-wave
@@ -835,12 +921,12 @@ bool fast_ok(int M, int NJ) {
 // 16-byte scale pieces, the block's scales fit the scale loads per lane,
 // at most NJ steps are in flight, and the LDS fits.
 template <int MODE, int R>
-bool slds_ok(int K, int NJ, int M, int64_t N) {
+bool slds_ok(int K, int NJ, int M, int64_t N, int64_t nblocks = -1) {
   const int cpr = K / 32;
   const int sarea = block_scale_bytes<MODE>(R, K);
   const int srb = sarea / (2 * R);
   if (cpr % 32 || srb % 16 || sarea > (MODE == BSFP_NVFP4 ? 4 : 2) * 1024 || steps_in_flight<R>() > NJ) return false;
-  return fast_shape<MODE, 1, R, true>(M, K, NJ, N).lds <= (size_t)device_max_lds();
+  return fast_shape<MODE, 1, R, true>(M, K, NJ, N, nblocks).lds <= (size_t)device_max_lds();
 }
 
 // The format variants: the same kernel with fewer launch shapes (2-row
@@ -1230,7 +1316,75 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
   return run<MODE, 8>(x, M, w, g2, y, s);
 }
 
+// Several matrices that share x, K and the format, one row of x: one launch
+// of the fast kernel with staged scales, chosen on their total rows as by_m
+// chooses on one matrix's rows; when that kernel does not take them, one
+// launch per matrix.
+template <int MODE>
+hipError_t by_m_batch(const uint16_t* x, const bsfp_qtensor* const* ws, uint16_t* const* ys,
+                      int count, hipStream_t s) {
+  const int K = (int)ws[0]->cols;
+  const int NJ = (int)((K / 32 + 31) / 32);
+  int64_t N = 0;
+  for (int i = 0; i < count; ++i) N += ws[i]->rows;
+  auto blocks = [&](int R) {
+    int64_t nb = 0;
+    for (int i = 0; i < count; ++i) nb += (ws[i]->rows + 2 * R - 1) / (2 * R);
+    return nb;
+  };
+  // two slots for two matrices (the kernel arguments grow with the slots,
+  // and a larger argument block measured slower per launch)
+  auto go = [&](auto r_c, auto nm_c) {
+    constexpr int R = decltype(r_c)::value, NM = decltype(nm_c)::value;
+    return launch_fast_mats<MODE, 1, R, false, true, false, NM>(x, 1, ws, ys, count, nullptr,
+                                                               NJ, s, 0);
+  };
+  using r1 = std::integral_constant<int, 1>;
+  using r2 = std::integral_constant<int, 2>;
+  using nm2 = std::integral_constant<int, 2>;
+  using nm4 = std::integral_constant<int, kQmvMats>;
+  if (fast_ok<MODE>(1, NJ) && K < (1 << 28) && N < (1 << 30)) {
+    const int64_t want = 8LL * device_cu_count();
+    if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, 1, N, blocks(2)))
+      return count == 2 ? go(r2{}, nm2{}) : go(r2{}, nm4{});
+    if (slds_ok<MODE, 1>(K, NJ, 1, N, blocks(1)))
+      return count == 2 ? go(r1{}, nm2{}) : go(r1{}, nm4{});
+  }
+  for (int i = 0; i < count; ++i) {
+    const hipError_t e = by_m<MODE>(x, 1, *ws[i], nullptr, ys[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_qmv_batch(const uint16_t* x, int M, const bsfp_qtensor* const* ws,
+                            uint16_t* const* ys, int count, hipStream_t s) {
+  const bsfp_qtensor* w2[kQmvMats];
+  uint16_t* y2[kQmvMats];
+  int n = 0;
+  for (int i = 0; i < count && i < kQmvMats; ++i) {
+    if (ws[i]->rows == 0) continue;  // nothing to compute
+    w2[n] = ws[i];
+    y2[n] = ys[i];
+    ++n;
+  }
+  if (n == 0) return hipGetLastError();
+  if (M == 1 && n > 1 && w2[0]->cols % 32 == 0) {
+    switch (format_id(w2[0]->mode, w2[0]->bits, w2[0]->group_size)) {
+      case FMT_AFF4_G64: return by_m_batch<FMT_AFF4_G64>(x, w2, y2, n, s);
+      case FMT_MXFP4: return by_m_batch<FMT_MXFP4>(x, w2, y2, n, s);
+      case FMT_NVFP4: return by_m_batch<FMT_NVFP4>(x, w2, y2, n, s);
+      default: break;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_qmv(x, M, *w2[i], y2[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 bool qmv_variant_supported(int M, const bsfp_qtensor& w) {
   if (w.cols % 32 != 0 || w.cols >= (1 << 28) || w.rows >= (1 << 30) || M < 1 || M > 8)

@@ -179,6 +179,28 @@ bsfp_status bsfp_qmv(const uint16_t* x, int64_t M, const bsfp_qtensor* w,
                      uint16_t* y, bsfp_stream stream);
 
 /*
+ * bsfp_qmv_batch: the decode GEMV of bsfp_qmv for `count` weight matrices
+ * that share x, y_i[m, n] = sum_k x[m, k] * dq(W_i)[n, k] for i < count,
+ * 1 <= count <= BSFP_QMV_BATCH_MAX.  A decoder's projections that read the
+ * same activations (gate and up of an MLP) are such a set; the decode
+ * weight stream the call serves is that of "epic: NVIDIA Volta (sm_70)
+ * inference acceleration program", Baseline (measured), qmv per layer.
+ * w[i] (host array of count descriptors) must share mode, bits, group size
+ * and K (cols); rows may differ.  y[i] (host array of count device pointers)
+ * is bf16 [M, w[i]->rows], 16-byte aligned.  With one row of x and a base
+ * format the matrices run as one launch (their rows dealt over the CUs
+ * together, so the launch's fixed start-up and drain are paid once); each
+ * output row is computed exactly as bsfp_qmv computes it.  Otherwise the
+ * matrices run one launch each.  Errors: BSFP_ERR_ARG for a count outside
+ * 1..BSFP_QMV_BATCH_MAX, null arrays or entries, descriptors that differ in
+ * mode, bits, group size or K, and everything bsfp_qmv rejects;
+ * BSFP_ERR_UNSUPPORTED as bsfp_qmv.  Nothing is launched on an error.
+ */
+#define BSFP_QMV_BATCH_MAX 4
+bsfp_status bsfp_qmv_batch(const uint16_t* x, int64_t M, const bsfp_qtensor* const* w,
+                           int32_t count, uint16_t* const* y, bsfp_stream stream);
+
+/*
  * bsfp_qmm_workspace_bytes: device scratch bytes that bsfp_qmm needs for
  * (mode, M, K, act): for BSFP_ACT_SAME, x's codes, scales and (NVFP4) amax
  * and g; 0 for BSFP_ACT_BF16.  Returns 0 for unsupported arguments.  The

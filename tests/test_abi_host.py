@@ -218,3 +218,33 @@ def test_noalloc_size_matches_header(blib):
     text = open(HEADER).read()
     m = re.search(r"#define BSFP_NOALLOC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == blib.NOALLOC_WORKSPACE_BYTES
+
+
+def test_qmv_batch_checks_before_touching_the_gpu(blib):
+    """bsfp_qmv_batch refuses a bad count, null arrays or entries, matrices
+    that differ in format or K, and what bsfp_qmv refuses, before launching."""
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    QP = C.POINTER(blib.QTensorDesc)
+
+    def call(descs, M=1, count=None, ys=None):
+        darr = (QP * max(1, len(descs)))(*[C.pointer(d) if d is not None else QP() for d in descs])
+        n = len(descs) if count is None else count
+        yarr = (C.c_void_p * max(1, len(descs)))(*([FAKE] * len(descs) if ys is None else ys))
+        return status(blib, L.bsfp_qmv_batch(X, M, darr, n, yarr, None))
+
+    a, b = desc(blib, rows=4, cols=256), desc(blib, rows=8, cols=256)
+    for n in (0, 5, -1):
+        assert call([a, b], count=n)[0] == "BSFP_ERR_ARG"
+    assert status(blib, L.bsfp_qmv_batch(X, 1, None, 1, None, None))[0] == "BSFP_ERR_ARG"
+    assert call([a, None])[0] == "BSFP_ERR_ARG"
+    st, msg = call([a, desc(blib, rows=4, cols=512)])
+    assert st == "BSFP_ERR_ARG" and "differs" in msg
+    st, msg = call([a, desc(blib, mode=1, group=32, rows=4, cols=256)])
+    assert st == "BSFP_ERR_ARG" and "differs" in msg
+    assert call([a, b], ys=[FAKE, None])[0] == "BSFP_ERR_ARG"
+    assert call([a, b], ys=[FAKE, FAKE + 8])[0] == "BSFP_ERR_ARG"  # not 16-byte aligned
+    assert call([a, b], M=9)[0] == "BSFP_ERR_ARG"
+    big = desc(blib, 3, 8, 32, rows=4, cols=1 << 16)
+    st, msg = call([big, big], M=2)
+    assert st == "BSFP_ERR_UNSUPPORTED" and "64 KB" in msg

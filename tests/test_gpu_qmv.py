@@ -245,3 +245,63 @@ def test_onehot_activations_rows(oracle_mod, bsfp, mode):
         assert np.all(np.abs(y - ref) <= np.abs(ref) * 2 ** -7 + 1e-30)
     else:
         assert np.array_equal(y, ref)
+
+
+# Several matrices that share x (bsfp_qmv_batch): one launch of the fast
+# kernel with rows of every matrix dealt over the CUs together.  Each row is
+# computed as bsfp_qmv computes it, so the outputs equal separate calls bit
+# for bit, and meet the oracle bar.
+def check_batch(o, b, x_bits, qos):
+    qds = [oracle_to_dev(b, o, qo) for qo in qos]
+    xd = to_dev(x_bits)
+    ys = b.qmv_batch(xd, qds)
+    singles = [b.qmv(xd, qd) for qd in qds]
+    torch.cuda.synchronize()
+    for y, y1, qo in zip(ys, singles, qos):
+        assert torch.equal(y, y1)
+        if y.numel() == 0:
+            continue
+        yref, den = o.matmul_wonly(x_bits, qo)
+        e = o.norm_err(from_dev(y), yref, den)
+        assert np.isfinite(e).all() and e.max() <= TOL, e.max()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_qmv_batch_ragged_matrices(oracle_mod, bsfp, mode):
+    """Row counts that end in partial blocks, 2 to 4 matrices; NVFP4 with a
+    different global scale per matrix (weights of different spread)."""
+    o = oracle_mod
+    K = 4096
+    x = S.generic((1, K), 1.0, seed=800, stream=mode)
+    qos = [o.quantize(mode, S.generic((n, K), sd, seed=801 + i, stream=mode))
+           for i, (n, sd) in enumerate([(96, 0.02), (37, 0.05), (200, 0.01), (3, 0.03)])]
+    check_batch(o, bsfp, x, qos[:2])
+    check_batch(o, bsfp, x, qos)
+
+
+def test_qmv_batch_skips_empty_matrices(oracle_mod, bsfp):
+    o = oracle_mod
+    K = 4096
+    x = S.generic((1, K), 1.0, seed=810)
+    qos = [o.quantize(2, S.generic((n, K), 0.02, seed=811 + n)) for n in (64, 0, 130)]
+    check_batch(o, bsfp, x, qos)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_qmv_batch_gate_up_full_size(oracle_mod, bsfp, mode):
+    """The decode gate and up projections at hidden 5120: two [25600, 5120]
+    matrices in one launch."""
+    o = oracle_mod
+    x = S.generic((1, 5120), 1.0, seed=820)
+    qos = [o.quantize(mode, S.generic((25600, 5120), 0.02, seed=821 + i)) for i in range(2)]
+    check_batch(o, bsfp, x, qos)
+
+
+@pytest.mark.parametrize("M", [2, 8])
+def test_qmv_batch_several_rows_of_x(oracle_mod, bsfp, M):
+    """With several rows of x the matrices run one launch each: same results
+    as separate calls."""
+    o = oracle_mod
+    x = S.generic((M, 2048), 1.0, seed=830 + M)
+    qos = [o.quantize(1, S.generic((n, 2048), 0.02, seed=831 + n)) for n in (70, 33)]
+    check_batch(o, bsfp, x, qos)
