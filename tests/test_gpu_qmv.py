@@ -305,3 +305,20 @@ def test_qmv_batch_several_rows_of_x(oracle_mod, bsfp, M):
     x = S.generic((M, 2048), 1.0, seed=830 + M)
     qos = [o.quantize(1, S.generic((n, 2048), 0.02, seed=831 + n)) for n in (70, 33)]
     check_batch(o, bsfp, x, qos)
+
+
+@pytest.mark.parametrize("case", ["mxfp8", "affine8_g32", "nvfp4_k_odd"])
+def test_qmv_batch_fallback_paths(oracle_mod, bsfp, case):
+    """Formats and shapes the matrix list does not take run one launch per
+    matrix: a format variant, and NVFP4 rows with K % 32 == 16."""
+    o = oracle_mod
+    K = 1040 if case == "nvfp4_k_odd" else 2048
+    x = S.generic((1, K), 1.0, seed=840, stream=K)
+    ws = [S.generic((n, K), 0.02, seed=841 + n) for n in (64, 45)]
+    if case == "mxfp8":
+        qos = [o.quantize(o.MXFP8, w) for w in ws]
+    elif case == "affine8_g32":
+        qos = [o.quantize(o.AFFINE, w, bits=8, group=32) for w in ws]
+    else:
+        qos = [o.quantize(2, w) for w in ws]
+    check_batch(o, bsfp, x, qos)
