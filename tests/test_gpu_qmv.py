@@ -322,3 +322,13 @@ def test_qmv_batch_fallback_paths(oracle_mod, bsfp, case):
     else:
         qos = [o.quantize(2, w) for w in ws]
     check_batch(o, bsfp, x, qos)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("N,K", [(200, 6144), (129, 5120), (77, 7168)])
+def test_qmv_step_counts(oracle_mod, bsfp, mode, N, K):
+    """One row of x with staged scales, rows of 5, 6 and 7 steps of 1024
+    elements on matrices with few rows per CU."""
+    x = S.generic((1, K), 1.0, seed=850 + K, stream=mode)
+    w = S.generic((N, K), 0.02, seed=851 + N, stream=mode)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
