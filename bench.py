@@ -6,7 +6,9 @@ already resident in HBM:
 
   act_quant   NVFP4 activation quantize X[4096,5120] (tensor amax + codes +
               E4M3 scales + global scale), 1 % outliers at +-20: a burst of
-              9 calls over 8 distinct copies of X (cold), per call
+              9 calls over 8 distinct copies of X (cold), per call; each call
+              is bsfp_quantize_ws (amax from per-workgroup partial maxima in
+              the tensor's workspace, two launches)
   act_quant_warm  the same, 8 calls on one X (warm), per call
   dequant     NVFP4 dequantize of the same tensor (burst of 8 calls, per call)
   w_quant     MXFP4 quantize W[5760,2880] and affine quantize W[1024,512]

@@ -30,12 +30,14 @@ ACT_BF16, ACT_SAME = 0, 1
 STATUS = {0: "BSFP_OK", 1: "BSFP_ERR_ARG", 2: "BSFP_ERR_UNSUPPORTED", 3: "BSFP_ERR_DEVICE"}
 
 EXPORTS = ("bsfp_amax", "bsfp_quantize", "bsfp_dequantize", "bsfp_qmv", "bsfp_qmv_batch",
-           "bsfp_quantize_sr", "bsfp_qmm_workspace_bytes", "bsfp_qmm",
+           "bsfp_quantize_sr", "bsfp_quantize_ws", "bsfp_qmm_workspace_bytes", "bsfp_qmm",
            "bsfp_qmm_dense_scratch_bytes",
            "bsfp_qmm_dense", "bsfp_qmm_noalloc", "bsfp_time_next_launch", "bsfp_last_error",
            "bsfp_version")
 # most matrices of one bsfp_qmv_batch call (BSFP_QMV_BATCH_MAX)
 QMV_BATCH_MAX = 4
+# bytes of bsfp_quantize_ws's workspace (BSFP_QUANTIZE_WS_BYTES)
+QUANTIZE_WS_BYTES = 1024
 # bytes of bsfp_qmm_noalloc's static device workspace (BSFP_NOALLOC_WORKSPACE_BYTES)
 NOALLOC_WORKSPACE_BYTES = 32 << 20
 
@@ -71,6 +73,7 @@ def lib():
             "bsfp_amax": (C.c_int, [P, I64, P, P]),
             "bsfp_quantize": (C.c_int, [P, QP, I32, P]),
             "bsfp_quantize_sr": (C.c_int, [P, QP, I32, P, P]),
+            "bsfp_quantize_ws": (C.c_int, [P, QP, I32, P, P, I64, P]),
             "bsfp_dequantize": (C.c_int, [QP, P, P]),
             "bsfp_qmv": (C.c_int, [P, I64, QP, P, P]),
             "bsfp_qmv_batch": (C.c_int, [P, I64, C.POINTER(QP), I32, C.POINTER(P), P]),
@@ -133,6 +136,9 @@ class QuantizedTensor:
     amax: Optional[torch.Tensor] = None          # fp32 [1] (NVFP4 tensor amax)
     bits: Optional[int] = None                   # None: the mode's (4; MXFP8 8)
     group: Optional[int] = None                  # None: the mode's group size
+    # uint8 [QUANTIZE_WS_BYTES] (NVFP4): the bsfp_quantize_ws workspace used
+    # when quantize() computes the global scale into this tensor
+    scratch: Optional[torch.Tensor] = None
 
     @property
     def group_size(self) -> int:
@@ -169,11 +175,12 @@ def empty_quantized(mode: int, rows: int, cols: int, device="cuda",
     scales = torch.empty((rows, cols // G), dtype=torch.uint8, device=device)
     if mode == MXFP8:
         return QuantizedTensor(mode, rows, cols, codes, scales, bits=bits, group=group)
-    gs = am = None
+    gs = am = ws = None
     if mode == NVFP4 and global_scale:
         gs = torch.empty(1, dtype=torch.float32, device=device)
         am = torch.empty(1, dtype=torch.float32, device=device)
-    return QuantizedTensor(mode, rows, cols, codes, scales, None, gs, am)
+        ws = torch.empty(QUANTIZE_WS_BYTES, dtype=torch.uint8, device=device)
+    return QuantizedTensor(mode, rows, cols, codes, scales, None, gs, am, scratch=ws)
 
 
 def _as_2d_bf16(x: torch.Tensor) -> torch.Tensor:
@@ -226,11 +233,14 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
              g: Optional[torch.Tensor] = None,
              out: Optional[QuantizedTensor] = None,
              rbits: Optional[torch.Tensor] = None, bits: Optional[int] = None,
-             group: Optional[int] = None) -> QuantizedTensor:
+             group: Optional[int] = None,
+             workspace: Optional[torch.Tensor] = None) -> QuantizedTensor:
     """Quantize a bf16 [rows, cols] GPU tensor.  For NVFP4, global_scale is
     'compute' (g = amax/2688), 'given' (use the fp32 [1] tensor g) or 'none'.
     rbits (uint32 words, one per element, NVFP4 / MXFP4): stochastic rounding
-    of the codes with those random words (bsfp_quantize_sr)."""
+    of the codes with those random words (bsfp_quantize_sr).  NVFP4 with
+    'compute' runs bsfp_quantize_ws on `workspace` (at least
+    QUANTIZE_WS_BYTES bytes), else on out.scratch, when there is one."""
     x2 = _as_2d_bf16(x)
     rows, cols = x2.shape
     gs = {"none": GS_NONE, "compute": GS_COMPUTE, "given": GS_GIVEN}[global_scale]
@@ -254,6 +264,13 @@ def quantize(x: torch.Tensor, mode: int, global_scale: str = "compute",
     if rbits is not None:
         if rbits.numel() != rows * cols or rbits.element_size() != 4 or not rbits.is_contiguous():
             raise ValueError("rbits needs one contiguous 32-bit word per element")
+    ws = workspace if workspace is not None else out.scratch
+    if mode == NVFP4 and gs == GS_COMPUTE and ws is not None:
+        ws = _buffer(ws, QUANTIZE_WS_BYTES, x.device, "workspace")
+        _check(lib().bsfp_quantize_ws(_ptr(x2), C.byref(d), gs, _ptr(rbits), _ptr(ws),
+                                      _nbytes(ws), _stream()))
+        return out
+    if rbits is not None:
         _check(lib().bsfp_quantize_sr(_ptr(x2), C.byref(d), gs if mode == NVFP4 else 0,
                                       _ptr(rbits), _stream()))
         return out

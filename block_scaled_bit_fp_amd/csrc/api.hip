@@ -195,9 +195,15 @@ bsfp_status bsfp_amax(const uint16_t* x, int64_t n, float* amax_out, bsfp_stream
   return device_status(launch_amax(x, n, amax_out, (hipStream_t)stream), "bsfp_amax");
 }
 
-// bsfp_quantize and bsfp_quantize_sr (rbits != nullptr: stochastic rounding).
+static_assert(BSFP_QUANTIZE_WS_BYTES == kAmaxParts * sizeof(float),
+              "the quantize workspace holds one partial maximum per amax workgroup");
+
+// bsfp_quantize, bsfp_quantize_sr (rbits != nullptr: stochastic rounding) and
+// bsfp_quantize_ws (parts != nullptr: NVFP4 GS_COMPUTE reduces the amax from
+// partial maxima there; checked by the caller).
 static bsfp_status quantize_impl(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
-                          const uint32_t* rbits, bsfp_stream stream, const char* fn) {
+                                 const uint32_t* rbits, bsfp_stream stream, const char* fn,
+                                 float* parts = nullptr) {
   bsfp_status st = check_qtensor(q, fn);
   if (st != BSFP_OK) return st;
   const int64_t n = q->rows * q->cols;
@@ -216,7 +222,10 @@ static bsfp_status quantize_impl(const uint16_t* x, const bsfp_qtensor* q, int32
   hipError_t e = hipSuccess;
   switch (q->mode) {
     case BSFP_NVFP4:
-      if (gs == BSFP_GS_COMPUTE) {
+      if (gs == BSFP_GS_COMPUTE && parts && n > 0) {
+        e = launch_amax_quantize_nvfp4(x, n, q->codes, (uint8_t*)q->scales, parts, q->amax,
+                                       q->global_scale, s, rbits);
+      } else if (gs == BSFP_GS_COMPUTE) {
         e = launch_amax(x, n, q->amax, s);
         if (e == hipSuccess)
           e = launch_quantize_nvfp4(x, n_words, q->codes, (uint8_t*)q->scales, q->amax, 1,
@@ -254,6 +263,32 @@ bsfp_status bsfp_quantize_sr(const uint16_t* x, const bsfp_qtensor* q, int32_t g
   if (q && q->rows * q->cols > 0 && (!rbits || !aligned16(rbits)))
     return fail(BSFP_ERR_ARG, "bsfp_quantize_sr: rbits is null or not 16-byte aligned");
   return quantize_impl(x, q, gs, rbits, stream, "bsfp_quantize_sr");
+}
+
+bsfp_status bsfp_quantize_ws(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                             const uint32_t* rbits, void* workspace, int64_t workspace_bytes,
+                             bsfp_stream stream) {
+  const char* fn = "bsfp_quantize_ws";
+  bsfp_status st = check_qtensor(q, fn);  // also bounds rows * cols
+  if (st != BSFP_OK) return st;
+  const bool nonempty = q->rows * q->cols > 0;
+  if (rbits) {  // the checks of bsfp_quantize_sr
+    if (q->mode != BSFP_NVFP4 && q->mode != BSFP_MXFP4)
+      return fail(BSFP_ERR_UNSUPPORTED,
+                  "%s: stochastic rounding applies to nvfp4 and mxfp4 only", fn);
+    if (nonempty && !aligned16(rbits))
+      return fail(BSFP_ERR_ARG, "%s: rbits is not 16-byte aligned", fn);
+  }
+  const bool uses_ws = q->mode == BSFP_NVFP4 && gs == BSFP_GS_COMPUTE;
+  if (uses_ws) {
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+      return fail(BSFP_ERR_ARG, "%s: workspace is null or not 4-byte aligned", fn);
+    if (workspace_bytes < BSFP_QUANTIZE_WS_BYTES)
+      return fail(BSFP_ERR_ARG, "%s: workspace of %lld bytes, %d needed", fn,
+                  (long long)workspace_bytes, (int)BSFP_QUANTIZE_WS_BYTES);
+  }
+  return quantize_impl(x, q, gs, rbits, stream, fn,
+                       uses_ws ? static_cast<float*>(workspace) : nullptr);
 }
 
 bsfp_status bsfp_dequantize(const bsfp_qtensor* q, uint16_t* out, bsfp_stream stream) {

@@ -60,6 +60,14 @@ hipError_t launch_quantize_dequant_nvfp4_bf16(const uint16_t* x, int64_t n_words
 constexpr int kAmaxParts = 256;
 hipError_t launch_amax_qdq_nvfp4_f16(const uint16_t* x, int64_t n, void* xhat, float* parts,
                                      float* amax_out, float* g_out, hipStream_t s);
+// NVFP4 quantize with g = amax/2688, the amax taken as for
+// launch_amax_qdq_nvfp4_f16 (partials in parts[kAmaxParts]; two launches, no
+// initialised memory, no atomics).  *amax_out and *g_out receive the tensor
+// amax and g.  n > 0, n % 16 == 0.
+hipError_t launch_amax_quantize_nvfp4(const uint16_t* x, int64_t n, uint32_t* codes,
+                                      uint8_t* scales, float* parts, float* amax_out,
+                                      float* g_out, hipStream_t s,
+                                      const uint32_t* rbits = nullptr);
 // MXFP4 quantize, then exact dequantization to bf16.
 hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words, void* xhat,
                                               hipStream_t s);

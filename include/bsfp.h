@@ -157,6 +157,30 @@ bsfp_status bsfp_quantize_sr(const uint16_t* x, const bsfp_qtensor* q, int32_t g
                              const uint32_t* rbits, bsfp_stream stream);
 
 /*
+ * bsfp_quantize_ws: bsfp_quantize (rbits == NULL) or bsfp_quantize_sr
+ * (rbits != NULL, with its requirements) with a caller workspace.  For
+ * NVFP4 with BSFP_GS_COMPUTE (the per-tensor global scale from the tensor
+ * amax: fp_quantize with a global scale, "mlx 0.30.7.3 -> 0.30.7.6",
+ * quantized.cpp and qqmm_utils.cu) the amax is reduced from per-workgroup
+ * partial maxima kept in the workspace instead of an atomic maximum whose
+ * accumulator a separate launch must zero first: two kernel launches
+ * instead of three, and the same bits (a maximum is exact in any order).
+ * Every other mode and gs ignores the workspace and behaves as
+ * bsfp_quantize / bsfp_quantize_sr.
+ *   workspace: device memory of at least BSFP_QUANTIZE_WS_BYTES bytes,
+ *   4-byte aligned, owned by the caller; its contents on entry are ignored
+ *   and undefined on return, and calls in flight at the same time need
+ *   separate workspaces.  May be NULL where it is ignored.
+ * Errors: those of bsfp_quantize / bsfp_quantize_sr, and BSFP_ERR_ARG for a
+ * needed workspace that is NULL, misaligned or smaller than
+ * BSFP_QUANTIZE_WS_BYTES.  Nothing is launched on an error.
+ */
+#define BSFP_QUANTIZE_WS_BYTES 1024
+bsfp_status bsfp_quantize_ws(const uint16_t* x, const bsfp_qtensor* q, int32_t gs,
+                             const uint32_t* rbits, void* workspace,
+                             int64_t workspace_bytes, bsfp_stream stream);
+
+/*
  * bsfp_dequantize: q -> bf16 out [q->rows, q->cols].  fp_dequantize /
  * affine_dequantize of "mlx 0.30.7.3 -> 0.30.7.6" (quantized.cpp).
  *   NVFP4  bf16((E2M1 * E4M3) * g)  (g = 1 when q->global_scale is NULL)

@@ -248,3 +248,33 @@ def test_qmv_batch_checks_before_touching_the_gpu(blib):
     big = desc(blib, 3, 8, 32, rows=4, cols=1 << 16)
     st, msg = call([big, big], M=2)
     assert st == "BSFP_ERR_UNSUPPORTED" and "64 KB" in msg
+
+
+def test_quantize_ws_checks_before_touching_the_gpu(blib):
+    """bsfp_quantize_ws needs its workspace only for NVFP4 with a computed
+    global scale, and refuses a missing, misaligned or short one; it keeps
+    bsfp_quantize_sr's checks when rbits is given."""
+    L = blib.lib()
+    X = C.c_void_p(FAKE)
+    need = blib.QUANTIZE_WS_BYTES
+    nv = desc(blib, gs=FAKE, amax=FAKE + 16)
+
+    def call(d, gs=1, rbits=None, ws=FAKE, nbytes=need):
+        return status(blib, L.bsfp_quantize_ws(X, C.byref(d), gs, rbits, ws, nbytes, None))
+
+    assert call(nv, ws=None)[0] == "BSFP_ERR_ARG"
+    assert call(nv, ws=FAKE + 2)[0] == "BSFP_ERR_ARG"
+    st, msg = call(nv, nbytes=need - 4)
+    assert st == "BSFP_ERR_ARG" and str(need) in msg
+    assert call(desc(blib, gs=FAKE))[0] == "BSFP_ERR_ARG"          # no amax buffer
+    assert call(nv, gs=7)[0] == "BSFP_ERR_ARG"                      # bad flag
+    assert call(desc(blib, cols=40, gs=FAKE, amax=FAKE))[0] == "BSFP_ERR_ARG"
+    assert call(nv, rbits=FAKE + 4)[0] == "BSFP_ERR_ARG"            # rbits misaligned
+    aff = desc(blib, mode=0, group=64, biases=FAKE)
+    assert call(aff, gs=0, rbits=FAKE, ws=None, nbytes=0)[0] == "BSFP_ERR_UNSUPPORTED"
+
+
+def test_quantize_ws_size_matches_header(blib):
+    text = open(HEADER).read()
+    m = re.search(r"#define BSFP_QUANTIZE_WS_BYTES (\d+)", text)
+    assert m and int(m.group(1)) == blib.QUANTIZE_WS_BYTES

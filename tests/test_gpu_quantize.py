@@ -55,6 +55,55 @@ def test_nvfp4_activation_config_bit_exact(oracle_mod, bsfp):
     assert qo.amax == np.float32(20.0)
 
 
+def _nvfp4_compute(b, xd, ws, rbits=None):
+    """NVFP4 quantize with the global scale computed: through bsfp_quantize_ws
+    when ws is a workspace tensor, through bsfp_quantize(_sr) when ws is None."""
+    q = b.empty_quantized(b.NVFP4, xd.shape[0], xd.shape[1], xd.device)
+    q.scratch = ws
+    return b.quantize(xd, b.NVFP4, out=q, rbits=rbits)
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (37, 64 * 13), (4096, 5120)])
+def test_nvfp4_compute_with_and_without_workspace(oracle_mod, bsfp, shape):
+    """The two-launch path (partial maxima in a caller workspace, whose stale
+    contents must not matter) and the three-launch path (zeroed atomic
+    accumulator) give the oracle's codes, scales, g and amax, bit for bit, with
+    nearest and with stochastic rounding."""
+    o = oracle_mod
+    x = S.nvfp4_activations(*shape, seed=220) if shape[0] > 1 else S.generic(shape, 1.0, seed=220)
+    r = S.random_words(shape, seed=221)
+    xd = to_dev(x)
+    rd = torch.from_numpy(np.ascontiguousarray(r).view(np.int32)).to("cuda")
+    ws = torch.full((bsfp.QUANTIZE_WS_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")  # NaNs
+    for rbits, words_r in ((None, None), (rd, r)):
+        qo = o.quantize(o.NVFP4, x, use_global=True, rbits=words_r)
+        for w in (ws, None):
+            q = _nvfp4_compute(bsfp, xd, w, rbits)
+            torch.cuda.synchronize()
+            tag = ("workspace" if w is not None else "atomic") + (" sr" if rbits is not None else "")
+            assert np.array_equal(words(q.codes), qo.codes), tag
+            assert np.array_equal(u8(q.scales), qo.scales), tag
+            assert q.amax.item() == qo.amax and q.global_scale.item() == qo.g, tag
+            ws.fill_(0xFF)
+
+
+def test_nvfp4_workspace_amax_planted_anywhere(bsfp):
+    """One element of magnitude 7.5 among values of magnitude <= 3.5, at the
+    first element, the middle, in the last workgroup's share and at the last
+    element: the workspace path's amax is exactly 7.5 and g = 7.5/2688."""
+    rows, cols = 4096, 5120
+    n = rows * cols
+    base = S.generic((n,), 1.0, seed=78)
+    base = (base & 0x8000) | np.minimum(base & 0x7FFF, 0x4060)
+    ws = torch.empty(bsfp.QUANTIZE_WS_BYTES, dtype=torch.uint8, device="cuda")
+    for pos in (0, n // 2 + 3, n - 4099, n - 1):
+        x = base.copy()
+        x[pos] = 0xC0F0  # bf16 -7.5
+        q = _nvfp4_compute(bsfp, to_dev(x.reshape(rows, cols)), ws)
+        assert q.amax.item() == 7.5, pos
+        assert q.global_scale.item() == np.float32(np.float32(7.5) / np.float32(2688.0)), pos
+
+
 def test_nvfp4_given_and_no_global_scale(oracle_mod, bsfp):
     x = S.generic((64, 1024), 0.02, seed=210)
     check_quant_exact(oracle_mod, bsfp, x, oracle_mod.NVFP4, gs="given", g=3.7e-5)
