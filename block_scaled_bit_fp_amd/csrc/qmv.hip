@@ -1197,45 +1197,56 @@ __global__ __launch_bounds__(512) void qmv_mma_kernel(
     }
   }
 
-  // the S partial tiles, added in wave order by the first RBW waves
+  // the S partial tiles of each 16-row block r, added in wave order by wave
+  // r % S (S may be smaller than RBW)
 #pragma unroll
   for (int r = 0; r < RBW; ++r) red[(w * RBW + r) * 64 + lane] = acc[r];
   __syncthreads();
-  if (w >= RBW) return;
-  const int r = w;
-  f32x4_t v = red[r * 64 + lane];
-  for (int q = 1; q < S; ++q) {
-    const f32x4_t o = red[(q * RBW + r) * 64 + lane];
-    v[0] += o[0];
-    v[1] += o[1];
-    v[2] += o[2];
-    v[3] += o[3];
-  }
   const float gs = ((MODE == FMT_NVFP4 && gptr) ? *gptr : 1.0f) * (g2ptr ? *g2ptr : 1.0f);
-  // output layout: lane (n = lane % 16, g) holds rows m = 4 g .. 4 g + 3
-  const int64_t n = n0 + 16 * r + c;
-  if (n < N) {
+  for (int r = w; r < RBW; r += S) {
+    f32x4_t v = red[r * 64 + lane];
+    for (int q = 1; q < S; ++q) {
+      const f32x4_t o = red[(q * RBW + r) * 64 + lane];
+      v[0] += o[0];
+      v[1] += o[1];
+      v[2] += o[2];
+      v[3] += o[3];
+    }
+    // output layout: lane (n = lane % 16, g) holds rows m = 4 g .. 4 g + 3
+    const int64_t n = n0 + 16 * r + c;
+    if (n < N) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = 4 * g + j;
-      if (m < M) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(v[j] * gs);
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g + j;
+        if (m < M) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(v[j] * gs);
+      }
     }
   }
 }
 
-// Launch shape of qmv_mma_kernel: RBW blocks of 16 rows per workgroup (two
-// for tall matrices, so that x is read once per 32 rows), and up to 8 waves
-// per workgroup splitting K, enough to put about 8 waves on every CU.
+// Launch shape of qmv_mma_kernel: RBW blocks of 16 rows per workgroup and S
+// <= 8 waves per workgroup splitting K, about 4 / RBW waves per CU.  Fewer,
+// longer waves keep more of each wave's K blocks behind the load ring.
+// The kernel is throughput-bound per CU, so a small matrix takes the RBW
+// that puts the fewest rows on the busiest CU (ceil(groups / CUs) * 16 RBW);
+// ties, and matrices of 2^25 weights or more, take RBW = 2 (x read once per
+// 32 rows).  By measurement at M = 8 ((RBW, S) -> us, MXFP4 unless noted):
+//   N = 4096 (256 groups of 16 rows: one per CU): (1, 4) 7.4, (2, 3) 8.8;
+//   N = 4224 (264 groups: 8 CUs take two): (1, 4) 11.1, (2, 3) 9.0;
+//   [5760, 2880]: (2, 3) 6.4, (1, 8) 8.3;  N = 8192: (2, 2) 9.2, (1, 4) 11.5;
+//   [5120, 25600] NVFP4: (2, 4) 40.6, (1, 8) 56.9, affine 52.0 / 71.6;
+//   [25600, 5120] NVFP4: (2, 1) 35.6, (2, 3) 36.8, (1, 1) 38.7.
+// NVFP4 and affine follow the same pattern on these shapes.
 template <int MODE>
 hipError_t launch_mma(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2,
                       uint16_t* y, hipStream_t s) {
   const int64_t N = w.rows;
   const int K = (int)w.cols;
   const int nkb = (K + 127) / 128;
-  const int want = 8 * device_cu_count();
   auto go = [&](auto rbw_c, auto odd_c) {
     constexpr int RBW = decltype(rbw_c)::value;
     constexpr bool ODD = decltype(odd_c)::value;
+    const int want = (RBW == 2 ? 2 : 4) * device_cu_count();
     const int64_t groups = (N + 16 * RBW - 1) / (16 * RBW);
     int S = (int)std::min<int64_t>(8, std::max<int64_t>(1, (want + groups - 1) / groups));
     S = std::min(S, nkb);
@@ -1250,25 +1261,30 @@ hipError_t launch_mma(const uint16_t* x, int M, const bsfp_qtensor& w, const flo
   using two = std::integral_constant<int, 2>;
   using odd = std::integral_constant<bool, true>;
   using even = std::integral_constant<bool, false>;
+  const int64_t cus = device_cu_count();
+  const int64_t rows1 = ((N + 15) / 16 + cus - 1) / cus * 16;   // busiest CU, RBW = 1
+  const int64_t rows2 = ((N + 31) / 32 + cus - 1) / cus * 32;   // RBW = 2
+  const bool rbw2 = N * K >= (int64_t(1) << 25) || rows2 <= rows1;
   // rows whose scale pairs are not aligned for one wider load: NVFP4 with
   // K % 32 == 16 (an odd number of scale bytes), affine with K % 128 == 64
   // (an odd number of groups)
   if constexpr (MODE == FMT_NVFP4 || MODE == FMT_AFF4_G64) {
     const bool odd_row = MODE == FMT_NVFP4 ? (K / 16) % 2 != 0 : (K / 64) % 2 != 0;
-    if (odd_row) return N >= 16384 ? go(two{}, odd{}) : go(one{}, odd{});
+    if (odd_row) return rbw2 ? go(two{}, odd{}) : go(one{}, odd{});
   }
-  return N >= 16384 ? go(two{}, even{}) : go(one{}, even{});
+  return rbw2 ? go(two{}, even{}) : go(one{}, even{});
 }
 
 // When the GEMV runs on MFMA (qmv_mma_kernel), by measurement on the
 // [25600, 5120], [5120, 25600], [5760, 2880] and [4096, 4096] shapes:
 // - x too large for the one LDS copy of the kernels below (which then walk
 //   K in slices): from 4 rows of x on, 1.1-3x faster;
-// - x in LDS: from 5 rows on, for matrices under 2^26 weights (1.2-1.4x
-//   faster); on larger ones the LDS kernels stream the weights faster up to
-//   the 64 KB limit of x (their loads touch fewer cache lines per
-//   instruction than the MFMA operand layout allows).
-constexpr int kMmaMinRows = 5;
+// - x in LDS: from 4 rows on, for matrices under 2^26 weights (MXFP4
+//   [5760, 2880] at M = 4: 6.7 against 8.8 us); on larger ones the LDS
+//   kernels stream the weights faster up to the 64 KB limit of x (their
+//   loads touch fewer cache lines per instruction than the MFMA operand
+//   layout allows; [25600, 5120] at M = 2..6: 1.1-1.7x).
+constexpr int kMmaMinRows = 4;
 constexpr int64_t kMmaLargeWeights = int64_t(1) << 26;
 
 template <int MODE, bool QX = false>
@@ -1280,7 +1296,7 @@ hipError_t by_m(const uint16_t* x, int M, const bsfp_qtensor& w, const float* g2
   if constexpr (!QX && (MODE == FMT_AFF4_G64 || MODE == FMT_MXFP4 || MODE == FMT_NVFP4)) {
     const bool x_lds = fast_ok<MODE>(M, NJ);
     const bool mma = x_lds ? (M >= kMmaMinRows && w.rows * w.cols < kMmaLargeWeights)
-                           : M >= kMmaMinRows - 1;
+                           : M >= kMmaMinRows;
     if (mma && w.cols < (1 << 26) && w.rows < (1 << 30)) return launch_mma<MODE>(x, M, w, g2, y, s);
   }
   if (fast_ok<MODE>(M, NJ) && w.cols < (1 << 28) && w.rows < (1 << 30)) {
