@@ -123,16 +123,36 @@ __device__ __forceinline__ float reduce_parts(const float* __restrict__ parts, i
 
 // ------------------------------------------------------------------ NVFP4
 
-// Two packed words per lane per step (lanes take words c + lane and
-// c + 256 + lane of a 512-word chunk c), both 16-byte loads issued before
-// either is used, on a grid of at most kNvfp4WgPerCu workgroups per CU that
-// strides over the chunks.  Fewer, longer workgroups pay the start-up (the
-// read of g or the reduction of the partial maxima, then a barrier) once per
-// workgroup slot instead of about four times: measured 20.8 us against 23.0
-// for X[4096, 5120] with g computed (one word per lane at 32 workgroups per
-// CU; one word at 8: 21.6; four words at 8: 21.7).
-constexpr int kNvfp4Words = 2;
+// The NVFP4 and MXFP4 quantizers take kQuantWords packed words per lane per
+// step: lane l takes words c + l and c + 256 + l of a chunk of 512 words c,
+// with both 16-byte loads issued before either is used, on a grid that
+// strides over the chunks with at most a few workgroups per CU.
+//   NVFP4, 8 workgroups per CU: fewer, longer workgroups pay the start-up
+// (the read of g or the reduction of the partial maxima, then a barrier)
+// once per workgroup slot instead of about four times; measured 20.8 us
+// against 23.0 for X[4096, 5120] with g computed (one word per lane at 32
+// workgroups per CU; one word at 8: 21.6; four words at 8: 21.7).
+//   MXFP4, 16 workgroups per CU: W[5760, 2880] 9.1 us against 10.2 (8: 9.4;
+// four words at 8: 9.6).  The same change to the dequantizer measured no
+// faster.
+constexpr int kQuantWords = 2;
 constexpr int kNvfp4WgPerCu = 8;
+constexpr int kMxfp4WgPerCu = 16;
+
+// Words c + u * kThreads + lane (u < kQuantWords) of x, zeros past n_words.
+__device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, int64_t c, int64_t n_words,
+                                           uint4 (&v)[kQuantWords]) {
+  if (c + (int64_t)kThreads * kQuantWords <= n_words) {
+#pragma unroll
+    for (int u = 0; u < kQuantWords; ++u) v[u] = x[c + u * kThreads + threadIdx.x];
+  } else {  // the last chunk
+#pragma unroll
+    for (int u = 0; u < kQuantWords; ++u) {
+      const int64_t i = c + u * kThreads + threadIdx.x;
+      v[u] = i < n_words ? x[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
 
 // rbits (stochastic rounding, NULL for nearest): 8 random words per packed
 // word, element order.
@@ -155,21 +175,12 @@ __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
   }
   if (g_out && blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
   const float six_g = 6.0f * g;
-  constexpr int64_t kChunk = (int64_t)kThreads * kNvfp4Words;
+  constexpr int64_t kChunk = (int64_t)kThreads * kQuantWords;
   for (int64_t c = (int64_t)blockIdx.x * kChunk; c < n_words; c += (int64_t)gridDim.x * kChunk) {
-    uint4 xv[kNvfp4Words];
-    if (c + kChunk <= n_words) {
+    uint4 xv[kQuantWords];
+    load_chunk(x, c, n_words, xv);
 #pragma unroll
-      for (int u = 0; u < kNvfp4Words; ++u) xv[u] = x[c + u * kThreads + threadIdx.x];
-    } else {  // the last chunk: words past n_words read as zeros, stored nowhere
-#pragma unroll
-      for (int u = 0; u < kNvfp4Words; ++u) {
-        const int64_t i = c + u * kThreads + threadIdx.x;
-        xv[u] = i < n_words ? x[i] : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kNvfp4Words; ++u) {
+    for (int u = 0; u < kQuantWords; ++u) {
       // n_words is even, so a lane pair (2j, 2j+1) is in or out together
       const int64_t i = c + u * kThreads + threadIdx.x;
       if (i >= n_words) break;
@@ -270,24 +281,32 @@ __global__ __launch_bounds__(kThreads) void quantize_dequant_nvfp4_kernel(
 __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
     const uint4* __restrict__ x, int64_t n_words, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const uint4* __restrict__ rbits) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;  // multiple of 4
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
-    float f[8];
-    unpack8(x[i], f);
-    float a = 0.0f;
+  constexpr int64_t kChunk = (int64_t)kThreads * kQuantWords;
+  for (int64_t c = (int64_t)blockIdx.x * kChunk; c < n_words; c += (int64_t)gridDim.x * kChunk) {
+    uint4 xv[kQuantWords];
+    load_chunk(x, c, n_words, xv);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
-    a = team_max<4>(a);  // 32-element group = 4 lanes
-    // floor(log2 a) = biased exponent - 127 for normal a; subnormal or zero
-    // a gives an exponent below -128, which the clamp maps to -127.
-    const int be = (int)(__float_as_uint(a) >> 23);
-    const int e = max(be - 129, -127);  // e <= 125 for finite bf16 input
-    const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
-    float v[8];
+    for (int u = 0; u < kQuantWords; ++u) {
+      // n_words is a multiple of 4, so a group's 4 lanes are in or out together
+      const int64_t i = c + u * kThreads + threadIdx.x;
+      if (i >= n_words) break;
+      float f[8];
+      unpack8(xv[u], f);
+      float a = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
-    codes[i] = rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v);
-    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+      for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(f[k]));
+      a = team_max<4>(a);  // 32-element group = 4 lanes
+      // floor(log2 a) = biased exponent - 127 for normal a; subnormal or zero
+      // a gives an exponent below -128, which the clamp maps to -127.
+      const int be = (int)(__float_as_uint(a) >> 23);
+      const int e = max(be - 129, -127);  // e <= 125 for finite bf16 input
+      const float p = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
+      codes[i] = rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v);
+      if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
+    }
   }
 }
 
@@ -516,11 +535,12 @@ int amax_parts_grid(int64_t n) {
                                 std::min(device_cu_count(), kAmaxParts));
 }
 
-// Workgroups of quantize_nvfp4_kernel over n_words packed words.
-int nvfp4_grid(int64_t n_words) {
-  constexpr int64_t chunk = (int64_t)kThreads * kNvfp4Words;
+// Workgroups of the quantizers that take kQuantWords words per lane, over
+// n_words packed words, at most wg_per_cu per CU.
+int chunk_grid(int64_t n_words, int wg_per_cu) {
+  constexpr int64_t chunk = (int64_t)kThreads * kQuantWords;
   const int64_t want = (n_words + chunk - 1) / chunk;
-  const int64_t cap = (int64_t)device_cu_count() * kNvfp4WgPerCu;
+  const int64_t cap = (int64_t)device_cu_count() * wg_per_cu;
   return (int)std::max<int64_t>(1, std::min(want, cap));
 }
 
@@ -546,7 +566,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax_out, hipStream_
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, const float* g_src, int g_src_is_amax,
                                  float* g_out, hipStream_t s, const uint32_t* rbits) {
-  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(nvfp4_grid(n_words)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(chunk_grid(n_words, kNvfp4WgPerCu)), dim3(kThreads), 0, s,
                      reinterpret_cast<const uint4*>(x), n_words, codes, scales, g_src,
                      g_src_is_amax, g_out, reinterpret_cast<const uint4*>(rbits),
                      (const float*)nullptr, 0, (float*)nullptr);
@@ -558,7 +578,7 @@ hipError_t launch_amax_quantize_nvfp4(const uint16_t* x, int64_t n, uint32_t* co
                                       float* g_out, hipStream_t s, const uint32_t* rbits) {
   const int grid = amax_parts_grid(n);
   hipLaunchKernelGGL(amax_parts_kernel, dim3(grid), dim3(kAmaxThreads), 0, s, x, n, parts);
-  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(nvfp4_grid(n / 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(chunk_grid(n / 8, kNvfp4WgPerCu)), dim3(kThreads), 0, s,
                      reinterpret_cast<const uint4*>(x), n / 8, codes, scales,
                      (const float*)nullptr, 0, g_out, reinterpret_cast<const uint4*>(rbits),
                      (const float*)parts, grid, amax_out);
@@ -606,7 +626,7 @@ hipError_t launch_quantize_dequant_mxfp4_bf16(const uint16_t* x, int64_t n_words
 
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t n_words, uint32_t* codes,
                                  uint8_t* scales, hipStream_t s, const uint32_t* rbits) {
-  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(n_words)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(chunk_grid(n_words, kMxfp4WgPerCu)), dim3(kThreads), 0, s,
                      reinterpret_cast<const uint4*>(x), n_words, codes, scales,
                      reinterpret_cast<const uint4*>(rbits));
   return hipGetLastError();
