@@ -246,9 +246,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     a_off[s] = r * K * 2 + swz(r, lane & 7) * 16;
   }
 
-  // B codes: 16-byte piece p of the tile's step is row p / 2, half p % 2;
-  // each wave loads PPW consecutive pieces.  Dense B: BROWS rows per wave,
-  // like A.
+  // B codes: LDS slot p of the tile's step holds row r = p / 2, half
+  // (p % 2) ^ ((r >> 3) & 1): rows 8..15 of every 16 swap their halves, so
+  // the 16 lanes of a phase of ds_read_b128 (16 consecutive rows, one half)
+  // fall on distinct banks (with the plain order rows r and r + 8 shared
+  // them: a 2-way conflict on every B read, 0.4 conflict cycles per LDS
+  // instruction of the qq main loop).  Each wave loads PPW consecutive
+  // slots.  Dense B: BROWS rows per wave, like A.
   constexpr int PPW = 2 * BN / NW;
   constexpr int BC_LOADS = (PPW + 63) / 64;
   static_assert(DENSE || (PPW * NW == 2 * BN && (PPW >= 64 ? PPW % 64 == 0 : 64 % PPW == 0)),
@@ -299,8 +303,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     for (int c = 0; c < BC_LOADS; ++c) {
       const int p0 = wave * PPW + c * 64;
       const int p = p0 + lane;
+      const int r = p >> 1;
       if (PPW >= 64 || lane < PPW)
-        buffer_load_lds16(rc, bc + p0, (p >> 1) * (K / 2) + (p & 1) * 16, k0 / 2);
+        buffer_load_lds16(rc, bc + p0, r * (K / 2) + ((p & 1) ^ ((r >> 3) & 1)) * 16, k0 / 2);
     }
     if (lane < SROWS) {
       const int so = (DEC == DEC_NVFP4 || DEC == DEC_NVFP4_F16) ? srow * srb + 4 * st
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dq_kernel(
     const uint8_t* bs = reinterpret_cast<const uint8_t*>(sb + A_U4 + BC_U4);
 #pragma unroll
     for (int j = 0; j < WNT; ++j) {
-      dst[j].codes = bc[nl[j] * 2 + h];
+      dst[j].codes = bc[nl[j] * 2 + (h ^ ((nl[j] >> 3) & 1))];
       if constexpr (DEC == DEC_NVFP4 || DEC == DEC_NVFP4_F16) {
         // two E4M3 bytes: blocks 2h and 2h + 1 of this 64-wide step
         dst[j].s0 = *reinterpret_cast<const uint16_t*>(bs + nl[j] * 4 + 2 * h);
