@@ -40,13 +40,29 @@ def test_affine_small_config(oracle_mod, bsfp):
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("N,K", [(37, 64 * 5), (300, 2880), (129, 5120), (17, 64 * 201)])
 def test_qmv_ragged(oracle_mod, bsfp, mode, M, N, K):
     if mode == 1 and K % 32:
         pytest.skip("K must be a multiple of 32")
     x = S.generic((M, K), 1.0, seed=300 + M, stream=K)
     w = S.generic((N, K), 0.02, seed=301 + mode, stream=N)
+    check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("M", [4, 8])
+@pytest.mark.parametrize("N,K", [(4200, 320), (4096, 1024), (8200, 448)])
+def test_mma_gemv_launch_shapes(oracle_mod, bsfp, mode, M, N, K):
+    """Several rows of x on the MFMA GEMV, on the launch shapes its rule
+    picks for small matrices (256 CUs): N = 4200 (32-row workgroups, one per
+    CU, the last with 8 rows), N = 4096 (one 16-row workgroup per CU) and
+    N = 8200 (16-row workgroups, up to three per CU, the last with 8 rows);
+    K with a partial last 128-element block (320, 448) and without (1024)."""
+    if mode == 0 and K % 64:
+        pytest.skip("affine K must be a multiple of 64")
+    x = S.generic((M, K), 1.0, seed=420 + M, stream=K)
+    w = S.generic((N, K), 0.02, seed=421 + mode, stream=N)
     check(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
 
 
