@@ -575,14 +575,16 @@ void launch_dense(const uint16_t* A, int M, const uint16_t* B, int N, int K, int
 
 // Dense bf16 GEMM y[M, N] = x . B^T on the same kernel (B bf16 [N, K]):
 // 256 x 256 tiles on 8 waves (128 x 64 per wave) with two 64 KB LDS stages
-// from kDenseBigRows rows of x up (5 % faster at M = 4096, 2 % slower at
-// M = 2048), else 256 x 128 tiles (128 x 32 per wave) with three 48 KB
-// stages.  As for the quantized GEMM, when the tiles fill the CUs for some
-// whole rounds plus a small last round (1600 tiles on 256 CUs at M = 2048
-// and 4096), the columns of the whole rounds run on the big tiles and the
-// rest as 128 x 64 tiles spread over all CUs: 602 -> 569 us at M = 2048,
-// 1049 -> 989 us at M = 4096 (whole dense call).
-constexpr int kDenseBigRows = 3072;
+// from kDenseBigRows rows of x up, else 256 x 128 tiles (128 x 32 per wave)
+// with three 48 KB stages.  As for the quantized GEMM, when the tiles fill
+// the CUs for some whole rounds plus a small last round, the columns of the
+// whole rounds run on the big tiles and the rest as 128 x 64 tiles spread
+// over all CUs.  Whole dense call on W[25600, 5120] (interleaved A/B, us):
+// the column split took M = 2048 from 602 to 569 and M = 4096 from 1049 to
+// 989; with it, the 256 x 256 tile beats 256 x 128 at every M measured from
+// 768 up (M = 768: 275 / 292, 1134: 358 / 394, 2048: 543 / 586, 2560: 628 /
+// 746).
+constexpr int kDenseBigRows = 768;
 
 hipError_t run_dense(const uint16_t* A, int M, const uint16_t* B, int N, int K, uint16_t* y,
                      hipStream_t s) {

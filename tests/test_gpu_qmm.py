@@ -347,15 +347,16 @@ def test_dense_ragged(oracle_mod, bsfp, mode, M, N, K):
     check_dense(oracle_mod, bsfp, x, oracle_mod.quantize(mode, w))
 
 
-# Dense tiles of 256 x 128: 2048 rows x 8448 columns make 8 x 66 = 528 tiles,
-# two whole rounds on 256 CUs plus 16 tiles, so the first 8192 columns run on
-# the big tiles and the last 256 on 128 x 64 tiles.  From 3072 rows the tiles
-# are 256 x 256: 3072 x 5632 make 12 x 22 = 264, one round plus 8 tiles
-# (5376 columns, then 256).  K = 1024 and 1088 (16 and 17 steps: both
-# remainders of the three-stage loop): at K of a few hundred |y| can come
-# close to sum_k |x_k w_k| for some of the 17M outputs, and the bf16 rounding
-# of the output alone (up to 2^-8 of |y|) then exceeds the 2.2e-3 bar.
-DENSE_SPLIT = [(2048, 8448, 1024), (2048, 8448, 1088), (3072, 5632, 1024)]
+# The dense path's column split.  From 768 rows the tiles are 256 x 256:
+# 2048 rows x 8448 columns make 8 x 33 = 264 tiles, one whole round on 256
+# CUs plus 8 tiles, so the first 8192 columns run on the big tiles and the
+# last 256 on 128 x 64 tiles.  Below 768 rows the tiles are 256 x 128: 512 x
+# 16896 make 2 x 132 = 264 (16384 columns, then 512).  K = 1024 and 1088 (16
+# and 17 steps: both remainders of the three-stage loop): at K of a few
+# hundred |y| can come close to sum_k |x_k w_k| for some of the outputs, and
+# the bf16 rounding of the output alone (up to 2^-8 of |y|) then exceeds the
+# 2.2e-3 bar.
+DENSE_SPLIT = [(2048, 8448, 1024), (2048, 8448, 1088), (512, 16896, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_SPLIT)
@@ -413,9 +414,9 @@ def test_dense_deterministic(bsfp):
 def test_dense_prefill_sampled_full_size(oracle_mod, bsfp, M):
     """X[M,5120] . W[25600,5120]^T (NVFP4, global scale) at full size: 64 full
     output rows plus 4096 random outputs against the oracle's dense
-    reference, computed one by one.  M = 4096 runs the 256 x 256 dense tile
-    with two LDS stages, the others the 256 x 128 tile; at M = 2048 and 4096
-    the last 1024 columns run on 128 x 64 tiles (the full rows cover them)."""
+    reference, computed one by one.  All three run the 256 x 256 dense tile
+    with two LDS stages; at M = 2048 and 4096 the last 1024 columns run on
+    128 x 64 tiles (the full rows cover them)."""
     o = oracle_mod
     x, w = S.nvfp4_prefill(M=M, N=25600, K=5120, seed=7)
     qo = o.quantize(2, w)
