@@ -634,13 +634,20 @@ hipError_t run_dq_big(const uint16_t* A, int M, const bsfp_qtensor& w, const flo
   return hipGetLastError();
 }
 
-// Tile shapes: 256 x 256 with 8 waves (each 128 x 64) for prefill row
-// counts; narrower M tiles for small M.
+// Tile shapes by the rows of x: 256 x 256 with 8 waves (each 128 x 64, the
+// ping-pong schedule) from 257 rows; below, tiles 128 columns wide, so that
+// a [25600, K] weight gives 200 workgroups rather than 100 for 256 CUs:
+// 64 x 128 up to 64 rows, 128 x 128 up to 128, 256 x 128 up to 256.  By
+// interleaved A/B on W[25600, 5120] (us, 256-wide tiles before): qq M = 64
+// 53.6 -> 42.0, M = 128 68.9 -> 49.0, M = 256 103.2 -> 76.0; weight-only
+// NVFP4 M = 128 68.4 -> 47.8, affine 83.3 -> 56.3.  At M = 320..512 the
+// 256 x 256 tiles stay ahead (qq M = 512: 115.5 against 142.9 on 256 x 128).
 template <int DEC>
 hipError_t run_dq_m(const uint16_t* A, int M, const bsfp_qtensor& w, const float* g1,
                     const float* g2, uint16_t* y, hipStream_t s) {
-  if (M <= 64) return run_dq<DEC, 1, 4, 2, 2>(A, M, w, g1, g2, y, s);
-  if (M <= 128) return run_dq<DEC, 2, 4, 2, 2>(A, M, w, g1, g2, y, s);
+  if (M <= 64) return run_dq<DEC, 1, 4, 2, 1>(A, M, w, g1, g2, y, s);
+  if (M <= 128) return run_dq<DEC, 2, 4, 2, 1>(A, M, w, g1, g2, y, s);
+  if (M <= 256) return run_dq<DEC, 2, 4, 4, 1>(A, M, w, g1, g2, y, s);
   return run_dq_big<DEC>(A, M, w, g1, g2, y, s);
 }
 

@@ -46,7 +46,7 @@ def check_qq(o, b, x, qo, tol=QQ_TOL):
     return y
 
 
-SHAPES = [(1, 70, 64), (37, 300, 320), (130, 257, 1024), (300, 513, 5120 // 4)]
+SHAPES = [(1, 70, 64), (37, 300, 320), (100, 385, 640), (130, 257, 1024), (300, 513, 5120 // 4)]
 
 
 @pytest.mark.parametrize("M,K", [(9, 64), (130, 1024), (2048, 5120)])
@@ -213,17 +213,18 @@ def _sampled_wonly(o, b, x, qo, seed):
     return o.norm_err(y[ai, bi], yref, den)
 
 
-@pytest.mark.parametrize("M", [1134, 2048, 4096])
+@pytest.mark.parametrize("M", [100, 200, 1134, 2048, 4096])
 def test_nvfp4_prefill_qq_sampled_full_size(oracle_mod, bsfp, M):
     """X[M,5120] x W[25600,5120]^T at full size: 64 full output rows plus
     4096 random outputs computed one by one by the oracle.  At M = 2048 and
     4096 the last 1024 output columns come from the second (small-tile)
-    launch; the full rows cover them."""
+    launch; the full rows cover them.  M = 100 and 200 run the tiles 128
+    columns wide (128 x 128 and 256 x 128, partial in M)."""
     e = _sampled_qq(oracle_mod, bsfp, M, 25600, 5120, seed=5)
     assert e.max() <= QQ_TOL, e.max()
 
 
-@pytest.mark.parametrize("M", [1134, 2048, 4096])
+@pytest.mark.parametrize("M", [200, 1134, 2048, 4096])
 def test_nvfp4_prefill_weight_only_sampled_full_size(oracle_mod, bsfp, M):
     """NVFP4 weight-only x[M,5120] . W[25600,5120]^T (bf16 x, W's global
     scale applied to the fp32 sums) at full size, sampled as above.  At
