@@ -1357,10 +1357,17 @@ hipError_t by_m_batch(const uint16_t* x, const bsfp_qtensor* const* ws, uint16_t
   };
   using r1 = std::integral_constant<int, 1>;
   using r2 = std::integral_constant<int, 2>;
+  using r4 = std::integral_constant<int, 4>;
   using nm2 = std::integral_constant<int, 2>;
   using nm4 = std::integral_constant<int, kQmvMats>;
   if (fast_ok<MODE>(1, NJ) && K < (1 << 28) && N < (1 << 30)) {
     const int64_t want = 8LL * device_cu_count();
+    // four rows per team once every CU gets 16 or more blocks of 8 rows: the
+    // gate+up pair of [25600, 5120] (51200 rows, 25 blocks per CU) measured
+    // 29.1 against 30.2 us (interleaved A/B, two boxes); one such matrix
+    // alone (12.5 blocks per CU) is faster with two rows per team
+    if (N >= 16 * want && slds_ok<MODE, 4>(K, NJ, 1, N, blocks(4)))
+      return count == 2 ? go(r4{}, nm2{}) : go(r4{}, nm4{});
     if (N >= 4 * want && slds_ok<MODE, 2>(K, NJ, 1, N, blocks(2)))
       return count == 2 ? go(r2{}, nm2{}) : go(r2{}, nm4{});
     if (slds_ok<MODE, 1>(K, NJ, 1, N, blocks(1)))

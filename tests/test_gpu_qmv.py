@@ -303,13 +303,25 @@ def test_qmv_batch_skips_empty_matrices(oracle_mod, bsfp):
     check_batch(o, bsfp, x, qos)
 
 
-@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_qmv_batch_gate_up_full_size(oracle_mod, bsfp, mode):
     """The decode gate and up projections at hidden 5120: two [25600, 5120]
-    matrices in one launch."""
+    matrices in one launch (51200 rows: four rows per team)."""
     o = oracle_mod
     x = S.generic((1, 5120), 1.0, seed=820)
     qos = [o.quantize(mode, S.generic((25600, 5120), 0.02, seed=821 + i)) for i in range(2)]
+    check_batch(o, bsfp, x, qos)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_qmv_batch_four_rows_per_team_ragged(oracle_mod, bsfp, mode):
+    """A batch of 33006 rows (four rows per team, blocks of 8 rows) whose
+    three matrices all end in a partial block: 20001, 13000 and 5 rows."""
+    o = oracle_mod
+    K = 2048
+    x = S.generic((1, K), 1.0, seed=840, stream=mode)
+    qos = [o.quantize(mode, S.generic((n, K), 0.02, seed=841 + i, stream=mode))
+           for i, n in enumerate((20001, 13000, 5))]
     check_batch(o, bsfp, x, qos)
 
 
