@@ -287,7 +287,10 @@ __global__ __launch_bounds__(kThreads) void qmv_nvfp4_words_kernel(
 // chunk loads per lane).  Deeper rings measured slower: on the affine
 // [5120, 25600] decode shape (one row per team) 20.3 us with 8 loads per lane
 // and 22.3 us with 16, against 18.9 us with 3; on [25600, 5120] (two rows per
-// team) 16.8 us with 8 against 16.2 us with 4.  The whole chip already keeps
+// team) 16.8 us with 8 against 16.2 us with 4.  Later interleaved A/B runs:
+// one row per team with 2 or 4 steps, 19.7 and 19.4 us against 19.2 with 3;
+// the gate+up batch at four rows per team with 1 or 3 steps, 29.8 us against
+// 28.8 with 2.  The whole chip already keeps
 // every row of such a matrix in flight at once.
 template <int R>
 constexpr int steps_in_flight() {
