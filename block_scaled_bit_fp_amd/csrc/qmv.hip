@@ -844,7 +844,15 @@ FastShape fast_shape(int M, int K, int NJ, int64_t N, int64_t nblocks = -1) {
   const int min_wpg = std::max(1, (units + kXu * 64 - 1) / (kXu * 64));
   const int64_t grid = std::min<int64_t>((int64_t)kPerCu * cus, nblocks);
   const int64_t passes = std::max<int64_t>(1, (nblocks + grid * kMaxW - 1) / (grid * kMaxW));
-  const int wpg = (int)std::min<int64_t>(
+  // One pass: every workgroup takes the most waves (the ones without a block
+  // only share the staging of x).  On the [5120, 25600] decode shape (10
+  // blocks and 51 KB of x per CU) 16 waves leave no room for the per-wave
+  // scale buffers next to x, so that launch reads its scales per chunk; by
+  // interleaved A/B (affine, us): staged scales on 13 waves 19.3, per-chunk
+  // scales on 13 waves 19.1, on 16 waves 18.9 (and 19.3-19.4 against
+  // 19.9-20.1 on two more boxes).  Several passes: the fewest waves that
+  // keep that many passes.
+  const int wpg = passes == 1 ? kMaxW : (int)std::min<int64_t>(
       kMaxW, std::max<int64_t>(min_wpg, (nblocks + grid * passes - 1) / (grid * passes)));
   size_t lds = fast_lds_bytes<MODE>(M, NJ) +
                (SLDS ? (size_t)wpg * slds_wave_bytes<MODE>(R, K) : 0);
