@@ -69,6 +69,63 @@ def test_qq_nvfp4_workspace_amax_and_g(oracle_mod, bsfp, M, K):
     assert head[1] == oracle_mod.global_scale(a)
 
 
+# Bytes before the fp16 activation operand in the NVFP4 qq workspace: amax
+# and g_x (256 B), then 256 partial maxima.
+NV_WS_HEAD = 256 + 256 * 4
+
+
+@pytest.mark.parametrize("M", [9, 1134, 2048, 4096, 6553, 6600])
+def test_qq_nvfp4_activation_operand_exact(oracle_mod, bsfp, M):
+    """The NVFP4 qq GEMM's activation operand, E2M1(code) * E4M3(S) as fp16
+    after the head of its workspace, equals the oracle's exact dequantization
+    of q(x) without g, value for value, and the head holds the oracle's amax
+    and g; from the smallest GEMM row count to 33.8 M elements."""
+    o = oracle_mod
+    K = 5120
+    x = S.nvfp4_activations(M, K, seed=600 + M)
+    w = S.generic((64, K), 0.02, seed=601)
+    qd = oracle_to_dev(bsfp, o, o.quantize(2, w))
+    ws = torch.full((bsfp.qmm_workspace_bytes(2, M, K, "same"),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    bsfp.qmm(to_dev(x), qd, act="same", workspace=ws)
+    torch.cuda.synchronize()
+    xhat = ws[NV_WS_HEAD:NV_WS_HEAD + M * K * 2].cpu().numpy().view(np.float16).reshape(M, K)
+    qx = o.quantize(o.NVFP4, x, use_global=True)
+    A = o.dequant_exact(qx, with_g=False)
+    assert np.array_equal(xhat.astype(np.float64), A)
+    head = ws[:8].cpu().numpy().view(np.float32)
+    assert head[0] == qx.amax and head[1] == qx.g
+
+
+def test_qq_nvfp4_graph_replay_matches_eager(oracle_mod, bsfp):
+    """The NVFP4 qq call (activation amax partials, quantize, GEMM) captured
+    in a HIP graph: three replays, with eager calls between them, each give
+    the eager call's output bit for bit."""
+    o = oracle_mod
+    M, K, N = 1134, 5120, 512
+    x = to_dev(S.nvfp4_activations(M, K, seed=610))
+    qd = oracle_to_dev(bsfp, o, o.quantize(2, S.generic((N, K), 0.02, seed=611)))
+    eager = bsfp.qmm(x, qd, act="same")
+    ws = torch.empty(bsfp.qmm_workspace_bytes(2, M, K, "same"), dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bsfp.qmm(x, qd, act="same", workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bsfp.qmm(x, qd, act="same", workspace=ws, out=out)
+    for r in range(3):
+        out.zero_()
+        graph.replay()
+        again = bsfp.qmm(x, qd, act="same")
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), r
+        assert torch.equal(again, eager), r
+
+
 @pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_weight_only_ragged(oracle_mod, bsfp, mode, M, N, K):

@@ -87,6 +87,28 @@ def test_nvfp4_compute_with_and_without_workspace(oracle_mod, bsfp, shape):
             ws.fill_(0xFF)
 
 
+@pytest.mark.parametrize("shape", [(3, 48), (512, 5120), (1134, 5120), (2048, 5120),
+                                   (4096, 8192), (4112, 8192)])
+def test_nvfp4_compute_workspace_shapes(oracle_mod, bsfp, shape):
+    """More shapes for the workspace path (partial maxima from one workgroup
+    per CU, then the quantize over a capped grid): a single 48-element row,
+    1 to 16 packed words per amax lane on 256 CUs, and a tensor of 33.7 M
+    elements.  Codes, scales, g and amax are bit-exact against the oracle,
+    and so is the atomic path."""
+    o = oracle_mod
+    x = S.nvfp4_activations(*shape, seed=230 + shape[0])
+    xd = to_dev(x)
+    ws = torch.full((bsfp.QUANTIZE_WS_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")  # NaNs
+    qo = o.quantize(o.NVFP4, x, use_global=True)
+    for w in (ws, None):
+        q = _nvfp4_compute(bsfp, xd, w, None)
+        torch.cuda.synchronize()
+        tag = "workspace" if w is not None else "atomic"
+        assert np.array_equal(words(q.codes), qo.codes), tag
+        assert np.array_equal(u8(q.scales), qo.scales), tag
+        assert q.amax.item() == qo.amax and q.global_scale.item() == qo.g, tag
+
+
 def test_nvfp4_workspace_amax_planted_anywhere(bsfp):
     """One element of magnitude 7.5 among values of magnitude <= 3.5, at the
     first element, the middle, in the last workgroup's share and at the last
