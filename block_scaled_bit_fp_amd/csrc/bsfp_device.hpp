@@ -330,6 +330,13 @@ __device__ __forceinline__ uint4 buffer_load_u128(rsrc_t r, int voff, int soff) 
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
+// The same load with the non-temporal cache policy (the `nt` bit, cache
+// policy 2 on gfx950), for data read once: a decode GEMV's weights.
+__device__ __forceinline__ uint4 buffer_load_u128_nt(rsrc_t r, int voff, int soff) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
 // s_waitcnt vmcnt(0): every vector-memory load of this wave has landed,
 // including the direct-to-LDS ones the compiler does not track.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -348,6 +355,17 @@ __device__ __forceinline__ void buffer_load_lds16(rsrc_t r, uint4* lds, int voff
   const uint32_t base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u4*)lds);
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
+               : "memory");
+}
+
+// The same with the non-temporal cache policy, for data read once.
+__device__ __forceinline__ void buffer_load_lds16_nt(rsrc_t r, uint4* lds, int voff, int soff) {
+  typedef __attribute__((address_space(3))) uint4 lds_u4;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u4*)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
                :
                : "v"(voff), "s"(r), "s"(soff), "{m0}"(base)
                : "memory");
