@@ -531,6 +531,17 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
     if constexpr (AFF) rbs = make_rsrc(pick<NM>(mats.biases, mi) + row0 * srb, rows * srb);
   };
   constexpr int SL = (MODE == BSFP_NVFP4) ? 4 : 2;
+  // 4-bit codes and their scales are read once, each load over whole cache
+  // lines: non-temporal loads (cache policy 2).  Decode sweep, interleaved
+  // A/B: the codes alone 46.0-46.2 against 48.1-48.5 us per layer (down
+  // 17.3 against 19.1, gate+up 28.0 against 29.0; the sc0 policy instead
+  // 47.2-47.9); the scales as well, one [25600, 5120] launch: NVFP4 15.3
+  // against 15.7, affine 15.6 against 16.1 us.  8-bit codes keep the
+  // default policy: a lane's 32 bytes come in two loads that split each
+  // cache line, and with nt the second fetches it again (MXFP8 [25600,
+  // 5120] fell from 5413 to 4657 GB/s).
+  constexpr bool kNt = BITS == 4;
+  constexpr int kPolicy = kNt ? 2 : 0;
   // fetch step j of the current block; `real` is false for the refills past
   // the wave's last step, `par` is the block's buffer
   auto fetch = [&](Chunk (&dst)[R], int j, bool real, int par) {
@@ -540,32 +551,37 @@ __global__ __launch_bounds__((fast_threads<MODE, MAXM>())) void qmv_fast_kernel(
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
           if (i < nsl) {
-            buffer_load_lds16_nt(rs, reinterpret_cast<uint4*>(b + i * 1024), 16 * lane + i * 1024, 0);
-            if constexpr (AFF)
-              buffer_load_lds16_nt(rbs, reinterpret_cast<uint4*>(b + sbuf + i * 1024),
-                                16 * lane + i * 1024, 0);
+            if constexpr (kNt) {
+              buffer_load_lds16_nt(rs, reinterpret_cast<uint4*>(b + i * 1024), 16 * lane + i * 1024, 0);
+              if constexpr (AFF)
+                buffer_load_lds16_nt(rbs, reinterpret_cast<uint4*>(b + sbuf + i * 1024),
+                                     16 * lane + i * 1024, 0);
+            } else {
+              buffer_load_lds16(rs, reinterpret_cast<uint4*>(b + i * 1024), 16 * lane + i * 1024, 0);
+              if constexpr (AFF)
+                buffer_load_lds16(rbs, reinterpret_cast<uint4*>(b + sbuf + i * 1024),
+                                  16 * lane + i * 1024, 0);
+            }
           }
         }
       }
     }
-    // codes and scales are read once: non-temporal loads (cache policy 2).
-    // Decode sweep, interleaved A/B: the codes alone 46.0-46.2 against
-    // 48.1-48.5 us per layer (down 17.3 against 19.1, gate+up 28.0 against
-    // 29.0; the sc0 policy instead: 47.2-47.9); the scales as well, one
-    // [25600, 5120] launch: NVFP4 15.3 against 15.7, affine 15.6 against
-    // 16.1 us.
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      dst[r].w = buffer_load_u128_nt(rc, vc[r], j * 32 * CB);
-      if constexpr (BITS == 8) dst[r].w2 = buffer_load_u128_nt(rc, vc[r] + 16, j * 32 * CB);
+      if constexpr (kNt) {
+        dst[r].w = buffer_load_u128_nt(rc, vc[r], j * 32 * CB);
+      } else {
+        dst[r].w = buffer_load_u128(rc, vc[r], j * 32 * CB);
+        if constexpr (BITS == 8) dst[r].w2 = buffer_load_u128(rc, vc[r] + 16, j * 32 * CB);
+      }
       if constexpr (!SLDS) {
         if constexpr (AFF) {
-          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 2);
-          dst[r].b = __builtin_amdgcn_raw_buffer_load_b16(rbs, vs[r], j * sstep, 2);
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, kPolicy);
+          dst[r].b = __builtin_amdgcn_raw_buffer_load_b16(rbs, vs[r], j * sstep, kPolicy);
         } else if constexpr (MX) {
-          dst[r].s = __builtin_amdgcn_raw_buffer_load_b8(rs, vs[r], j * sstep, 2);
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b8(rs, vs[r], j * sstep, kPolicy);
         } else {
-          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, 2);
+          dst[r].s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[r], j * sstep, kPolicy);
         }
       }
     }
