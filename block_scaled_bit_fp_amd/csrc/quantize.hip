@@ -33,22 +33,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Non-temporal 16-byte load and store (the `nt` cache policy): the
-// streaming kernels below read their input and write their output once.
-// Interleaved A/B against plain accesses: X[4096, 5120] activation quantize
-// (cold) 19.8-20.1 against 20.7-21.1 us, MXFP4 W[5760, 2880] quantize
-// 9.2-9.4 against 10.1-10.4 us, NVFP4 [4096, 5120] dequantize 10.3 against
-// 12.9-13.0 us; bit-identical outputs.
-typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_nt(const uint4* p) {
-  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void store16_nt(uint4 o, uint4* p) {
-  const u32x4_nt v = {o.x, o.y, o.z, o.w};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
-}
-
 // ------------------------------------------------------------------ amax
 
 __global__ void amax_init_kernel(float* out) { *out = 0.0f; }
@@ -160,12 +144,12 @@ __device__ __forceinline__ void load_chunk(const uint4* __restrict__ x, int64_t 
                                            uint4 (&v)[kQuantWords]) {
   if (c + (int64_t)kThreads * kQuantWords <= n_words) {
 #pragma unroll
-    for (int u = 0; u < kQuantWords; ++u) v[u] = load16_nt(&x[c + u * kThreads + threadIdx.x]);
+    for (int u = 0; u < kQuantWords; ++u) v[u] = x[c + u * kThreads + threadIdx.x];
   } else {  // the last chunk
 #pragma unroll
     for (int u = 0; u < kQuantWords; ++u) {
       const int64_t i = c + u * kThreads + threadIdx.x;
-      v[u] = i < n_words ? load16_nt(&x[i]) : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = i < n_words ? x[i] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
@@ -223,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void quantize_nvfp4_kernel(
       } else {
         S = 0;
       }
-      __builtin_nontemporal_store(w, &codes[i]);
-      if ((i & 1) == 0) __builtin_nontemporal_store((uint8_t)S, &scales[i >> 1]);
+      codes[i] = w;
+      if ((i & 1) == 0) scales[i >> 1] = (uint8_t)S;
     }
   }
 }
@@ -320,8 +304,7 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = f[k] * p;
-      __builtin_nontemporal_store(
-          rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v), &codes[i]);
+      codes[i] = rbits ? e2m1_pack8_sr(v, rbits[2 * i], rbits[2 * i + 1]) : e2m1_pack8(v);
       if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(e + 127);
     }
   }
@@ -383,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const float g = gptr ? *gptr : 1.0f;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_words; i += stride) {
-    const uint32_t w = __builtin_nontemporal_load(&codes[i]);
+    const uint32_t w = codes[i];
     float v[8];
     if constexpr (MODE == BSFP_AFFINE) {
       const float s = bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[i >> 3]);
@@ -411,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     o.y = pack_bf16x2(v[2], v[3]);
     o.z = pack_bf16x2(v[4], v[5]);
     o.w = pack_bf16x2(v[6], v[7]);
-    store16_nt(o, &out[i]);
+    out[i] = o;
   }
 }
 
